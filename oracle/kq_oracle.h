@@ -1,0 +1,80 @@
+/*
+ * CPU oracle for the KroQuant online activation quantizer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link or
+ * call this: only the tests, the smoke check and the CPU-baseline leg of the
+ * benchmark use it.  It shares no code with the HIP library.
+ *
+ * Plain, single-threaded, fp64 where the arithmetic is floating point.  The
+ * method (KroQuant, arXiv 2607.21446, as read from the Pith review page,
+ * "What carries the argument", referee report on Sec. 3.2 Eqs. (4)-(6), and
+ * the original abstract):
+ *   - a block-diagonal transform T applied to the activations, one 32x32
+ *     block K(j) per 32 channels, K = G1 (x) G2 (x) G3 (x) G4 (x) G5;
+ *   - each G_k a 2x2 unit-determinant LU factor with three scalars;
+ *   - the transformed activations quantized to MXFP4 (E2M1 elements, one
+ *     E8M0 scale per 32 elements; OCP Microscaling Formats v1.0, reference
+ *     [10] of the same page).
+ * Readings of points the pages leave open are listed next to each function.
+ */
+#ifndef KQ_ORACLE_H
+#define KQ_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { KQO_KRON = 0, KQO_PLAIN = 1, KQO_SMOOTH = 2, KQO_HADAMARD = 3 };
+
+/* G = L U with L = [[1,0],[l,1]], U = [[a,b],[0,1/a]], row-major G[0..3]. */
+void kqo_factor(float l, float a, float b, double G[4]);
+/* Closed-form inverse [[l b + 1/a, -b], [-l a, a]] of the factor above. */
+void kqo_factor_inverse(float l, float a, float b, double Gi[4]);
+/* K = G1 (x) ... (x) G5 from the index bits: K[r][c] = prod_k G_k[bit(r)][bit(c)]. */
+void kqo_kron_dense(const float P[15], double K[1024]);
+/* The same K, built by pushing each unit row vector through 5 butterfly stages. */
+void kqo_kron_butterfly(const float P[15], double K[1024]);
+/* (G1^-1) (x) ... (x) (G5^-1). */
+void kqo_kron_inverse(const float P[15], double Kinv[1024]);
+/* K rounded to fp32, row-major [r][c] (row r = input channel, c = output channel). */
+void kqo_block_f32(const float P[15], float K32[1024]);
+/*
+ * Dense blocks for nb blocks, params read at P + j*pstride (pstride 15 or 0).
+ * K32: [nb][32 r][32 c] fp32 (may be NULL).
+ * Kbf: [nb][n_split][32 c][32 r] bf16 bit patterns, transposed, the terms
+ *      hi = bf16(K32), mid = bf16(K32 - hi), lo = bf16(K32 - hi - mid) (may be NULL).
+ */
+void kqo_build_blocks(const float* P, int64_t nb, int64_t pstride, float* K32, uint16_t* Kbf, int n_split);
+
+/* E2M1 magnitude index (0..7) of |v| under round-to-nearest-even with saturation. */
+int kqo_e2m1_index(double m);
+/* E8M0 scale byte for a block amax: floor(log2 amax) - 2 + 127 clamped to [0, 254]; amax == 0 -> 0. */
+uint8_t kqo_e8m0(float amax);
+/* Quantize one block of 32 fp32 values: 16 packed code bytes + 1 scale byte. */
+void kqo_quantize_block(const float y[32], uint8_t codes[16], uint8_t* scale);
+
+/*
+ * Whole path for rows [row0, row1) of X[T][d] (bf16 bits):
+ *   front = KQO_KRON     y = x K(j), params at P + j*pstride
+ *           KQO_PLAIN    y = x
+ *           KQO_SMOOTH   y = fp32(x * m[c])
+ *           KQO_HADAMARD y = fp32((x H32)[c] / sqrt(32)), H32[r][c] = (-1)^popcount(r & c)
+ * Outputs are written for the requested rows only, starting at row 0 of each
+ * output: codes [(row1-row0)][d/2], scales [(row1-row0)][d/32], and when not
+ * NULL y32 (the fp32 values that were quantized) and yhat (the fp64 value
+ * before the final rounding).  Returns 0, or 1 on bad arguments.
+ */
+int kqo_quantize_rows(int front, const uint16_t* X, int64_t T, int64_t d, const float* P, int64_t pstride,
+                      const float* m, int64_t row0, int64_t row1, uint8_t* codes, uint8_t* scales, float* y32,
+                      double* yhat);
+
+/* Fast Walsh-Hadamard transform of 32 values in place (natural order, unnormalized). */
+void kqo_fwht32(double v[32]);
+/* Determinant of an n x n fp64 matrix by LU with partial pivoting. */
+double kqo_det(const double* A, int n);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
