@@ -1,0 +1,212 @@
+"""Benchmark of the KroQuant online activation quantizer on one MI355X.
+
+One step = the streaming-stress workload: 57 back-to-back kq_quantize calls on
+a bf16 activation X[18432 x 12288] (FLUX.1-schnell width, 4 x 4608 tokens),
+alternating two input and two output buffer sets so that nothing is served
+from the 256 MB Infinity Cache.  Throughput counts the algorithmic bytes of
+the path, 2 B in + 0.5 B codes + 1/32 B scales per element (parameters, 23 KB
+per call, excluded).  Inputs are resident in HBM before timing starts.
+
+Prints one JSON line (rank 0).  Also reported in the same line: the three
+comparison kernels and the other two KroQuant variants on the same inputs,
+the roofline position of the dominant kernel, and the CPU oracle's rate.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "transform+MXFP4 quantize GB/s and % of MI355X HBM peak; Gelem/s per shape"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD public specification
+BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0
+CALLS = 57
+KERNEL_SOURCES = ["kq_device.hpp", "kq_mfma.hip", "kq_quad.hip", "kq_api.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "w4a4_diffusion_transformer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--variant", default="auto", choices=["auto", "mfma_dense", "mfma_otf", "butterfly"])
+    ap.add_argument("--no-compare", action="store_true", help="skip the comparison kernels")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--profile-pass", action="store_true",
+                    help="few launches of each kernel plus a plain copy of known size, for rocprofv3 counter runs")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the quantizer needs no communication and this build runs on a single "
+              "MI355X; multi-GPU sharding is described in DESIGN.md, not run.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import w4a4_diffusion_transformer_amd as kq
+
+    dev = torch.device("cuda:0")
+    spec = synth.CONFIGS[4][0]
+    T, d = spec.T, spec.d
+    nb = d // 32
+    n = T * d
+    t0 = time.time()
+    X = synth.matrix(spec)
+    P = synth.params(spec)
+    m = synth.smooth_mult(X)
+    print(f"# generated {T}x{d} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    Xs = [torch.from_numpy(X.view(np.int16)).to(dev)]
+    Xs.append(Xs[0].clone())
+    Pd = torch.from_numpy(P).to(dev)
+    md = torch.from_numpy(m).to(dev)
+    outs = [kq.alloc_outputs(Xs[0]) for _ in range(2)]
+    Kbf = torch.empty((nb, 3, 32, 32), dtype=torch.int16, device=dev)
+    kq.kq_build_blocks(Pd, nb, None, Kbf, 3)
+    torch.cuda.synchronize()
+
+    def kron(v):
+        if v == kq.KQ_MFMA_DENSE:
+            return lambda i: kq.kq_quantize_ex(Xs[i & 1], None, 15, Kbf, v, *outs[i & 1])
+        if v == kq.KQ_AUTO:
+            return lambda i: kq.kq_quantize(Xs[i & 1], Pd, *outs[i & 1])
+        return lambda i: kq.kq_quantize_ex(Xs[i & 1], Pd, 15, None, v, *outs[i & 1])
+
+    def step(call):
+        for i in range(CALLS):
+            call(i)
+
+    def timed(call, steps, warmup):
+        for _ in range(warmup):
+            step(call)
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(steps):
+            step(call)
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e)  # ms
+
+    main_v = kq.VARIANTS[args.variant]
+    if args.profile_pass:
+        for _ in range(3):
+            kron(main_v)(0)
+        for v in (kq.KQ_MFMA_DENSE, kq.KQ_MFMA_OTF, kq.KQ_BUTTERFLY):
+            kron(v)(1)
+        kq.kq_smooth_quantize(Xs[0], md, *outs[0])
+        kq.kq_mx_quantize(Xs[0], *outs[0])
+        kq.kq_hadamard_quantize(Xs[0], *outs[0])
+        # plain copy kernel of known size for counter calibration: 1 GiB read + 1 GiB written
+        a = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_pass": True, "copy_bytes": a.numel() * 2}))
+        return
+
+    ms = timed(kron(main_v), args.steps, args.warmup)
+    ms_step = ms / args.steps
+    bytes_call = BYTES_PER_ELEM * n
+    gbs = bytes_call * CALLS * args.steps / (ms * 1e-3) / 1e9
+    launch_us = ms * 1e3 / (args.steps * CALLS)
+
+    comparison = {}
+    if not args.no_compare:
+        def rate(call):
+            t = timed(call, max(2, args.steps // 2), 1)
+            return round(bytes_call * CALLS * max(2, args.steps // 2) / (t * 1e-3) / 1e9, 1)
+
+        for name, v in (("mfma_dense", kq.KQ_MFMA_DENSE), ("mfma_otf", kq.KQ_MFMA_OTF),
+                        ("butterfly", kq.KQ_BUTTERFLY)):
+            comparison[f"kroquant_{name}_GBps"] = rate(kron(v))
+        comparison["smoothquant_mxfp4_GBps"] = rate(lambda i: kq.kq_smooth_quantize(Xs[i & 1], md, *outs[i & 1]))
+        comparison["plain_mxfp4_GBps"] = rate(lambda i: kq.kq_mx_quantize(Xs[i & 1], *outs[i & 1]))
+        comparison["hadamard32_mxfp4_GBps"] = rate(lambda i: kq.kq_hadamard_quantize(Xs[i & 1], *outs[i & 1]))
+        comparison["kroquant_time_over_smoothquant_time"] = round(comparison["smoothquant_mxfp4_GBps"] / gbs, 4)
+        comparison["pages_context"] = ("KroQuant quantizer up to 14% faster than the SmoothQuant kernel on an MI350 "
+                                       "(Triton); another machine, context only")
+
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+
+        rows = int(os.environ.get("KQ_CPU_SAMPLE_ROWS", "4096"))
+        t1 = time.perf_counter()
+        oracle.quantize_rows(oracle.KRON, X[:rows], P, threads=1)
+        dt = time.perf_counter() - t1
+        cpu = {"value": round(BYTES_PER_ELEM * rows * d / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"first {rows} of {T} rows of the stress matrix (d={d}), one call, single thread, "
+                         f"{dt:.1f} s"}
+
+    variant_name = args.variant
+    kernel = {"auto": "mfma_otf", "mfma_dense": "mfma_dense", "mfma_otf": "mfma_otf",
+              "butterfly": "butterfly"}[variant_name]
+    traffic = load_traffic(kernel, "stress")
+    roofline = {"bound": "hbm", "achieved": round(bytes_call / (launch_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(bytes_call / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel": f"kq {kernel}", "avg_launch_us": round(launch_us, 2),
+                "algorithmic_bytes_per_launch": int(bytes_call)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"stress: X[{T} x {d}] bf16 Student-t(3), 1% outlier channels x200, 1% zero blocks; "
+                               f"{CALLS} back-to-back kq_quantize calls per step",
+                   "tokens": T, "d": d, "calls_per_step": CALLS, "variant": variant_name,
+                   "gelem_per_s": round(n * CALLS * args.steps / (ms * 1e-3) / 1e9, 1),
+                   "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "comparison": comparison,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,181 @@
+/*
+ * kq.h - C ABI of libkq, the MI355X (gfx950) KroQuant online activation
+ * quantizer.
+ *
+ * What it computes.  KroQuant (arXiv 2607.21446; read from the Pith review
+ * page, "What carries the argument", core claim, and the referee report on
+ * Sec. 3.2 Eqs. (4)-(6); and the AIssential summary page) quantizes the input
+ * X[tokens][d] of a DiT linear layer to W4A4's activation side as follows:
+ *   1. every 32-channel block j of a row is multiplied on the right by its
+ *      own invertible 32x32 matrix K(j) = G1 (x) G2 (x) G3 (x) G4 (x) G5, a
+ *      Kronecker product of five 2x2 unit-determinant LU factors
+ *      G = [[1,0],[l,1]] [[a,b],[0,1/a]] = [[a, b], [l a, l b + 1/a]]
+ *      (three scalars per factor, 15 per block); y = x K(j) in the
+ *      row-vector convention of the review's Eq. (1);
+ *   2. each transformed block of 32 is quantized to MXFP4 (OCP Microscaling
+ *      Formats v1.0, the review's reference [10]): one E8M0 scale byte
+ *      e + 127 with e = floor(log2 amax) - 2 (amax = 0 -> byte 0; clamped to
+ *      [-127, 127]), and 32 E2M1 codes of y / 2^e rounded to nearest with
+ *      ties to the even code and saturation at +-6; bit 3 of a code is the
+ *      sign of y.
+ * The pages compare this quantizer with a per-channel (SmoothQuant) scale and
+ * a fixed Hadamard transform at the same block size (review, "If this is
+ * right"; original abstract); those two, and a plain MXFP4 quantizer, are
+ * here too with the same output format.
+ *
+ * Layouts (all row-major, little-endian):
+ *   X         bf16 bit patterns [tokens][d], d a positive multiple of 32.
+ *   K_params  fp32 [nb][5][3] (nb = d/32): (l, a, b) of G1 .. G5 for block j
+ *             at K_params + j * params_block_stride (stride 15, or 0 for one
+ *             K shared by every block).  a must be nonzero and finite.
+ *   K_f32     fp32 [nb][32][32], K[r][c] (r = input channel, c = output).
+ *   K_bf16    bf16 bit patterns [nb][n_split][32][32], TRANSPOSED: entry
+ *             [j][s][c][r]; the terms hi = bf16(K), mid = bf16(K - hi),
+ *             lo = bf16(K - hi - mid), each rounded to nearest even.  With
+ *             three terms hi + mid + lo equals the fp32 K exactly.
+ *   codes     uint8 [tokens][d/2]; byte q of block j holds the codes of
+ *             channels 32j+2q (low nibble) and 32j+2q+1 (high nibble).
+ *   scales    uint8 [tokens][d/32], E8M0 (2^(byte-127)).
+ *   ch_mult   fp32 [d] per-channel multipliers (SmoothQuant: 1/s_c).
+ *   Y         fp32 [tokens][d], the values the quantizer rounded.
+ *
+ * Numerics.  The transform runs in fp32 (MFMA bf16 products of X with a
+ * three-term bf16 split of K, or fp32 butterfly stages); the per-element
+ * error against the exact sum is below 1e-5 of the block amax.  Whenever a
+ * block's amax lands within 2^-16 (relative) of a power of two, the columns
+ * that decide the scale are recomputed exactly (fp64 sum of exact products,
+ * the fp32 K), so the E8M0 scales equal those of an exact evaluation.  An
+ * E2M1 code can differ from the exact evaluation's only where y / 2^e lies
+ * within that error of a rounding midpoint.  Plain and SmoothQuant
+ * front-ends are exact.
+ *
+ * Ownership and streams.  The caller owns every buffer (device memory, e.g.
+ * PyTorch tensors).  The library allocates nothing, frees nothing, keeps no
+ * pointer after returning and never synchronizes: each call only enqueues
+ * kernels on `stream` (NULL = the null stream) and returns.  Outputs must not
+ * overlap inputs.  Reentrant and thread-safe; the only shared state is a
+ * per-device cache of the compute-unit count, filled on first use.
+ *
+ * Errors.  Argument checks run before any HIP call and write nothing:
+ *   KQ_ERR_NULL    a required pointer is NULL while tokens > 0;
+ *   KQ_ERR_SHAPE   d <= 0, d % 32 != 0, tokens < 0, tokens * d >= 2^40,
+ *                  nb <= 0, n_split not in 1..3, a stride other than 15 / 0;
+ *   KQ_ERR_ALIGN   X, codes, Y, K_bf16, ch_mult not 16-byte aligned, or
+ *                  K_params / K_f32 not 4-byte aligned;
+ *   KQ_ERR_VARIANT unknown variant, or a variant whose inputs are missing
+ *                  (KQ_MFMA_DENSE needs K_bf16; the others need K_params);
+ *   KQ_ERR_ALIAS   an output range overlaps an input range or another output.
+ * tokens == 0 returns KQ_OK without touching the GPU.  A failed launch
+ * returns KQ_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ * synchronization, as for any asynchronous HIP work.  No C++ exception
+ * crosses this boundary.
+ */
+#ifndef KQ_H
+#define KQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+typedef enum {
+  KQ_OK = 0,
+  KQ_ERR_NULL = 1,
+  KQ_ERR_SHAPE = 2,
+  KQ_ERR_ALIGN = 3,
+  KQ_ERR_VARIANT = 4,
+  KQ_ERR_HIP = 5,
+  KQ_ERR_ALIAS = 6
+} kq_status;
+
+/* How K is applied.  AUTO picks per shape (documented in kq_api.hip). */
+typedef enum {
+  KQ_AUTO = 0,
+  KQ_MFMA_DENSE = 1, /* MFMA bf16 contraction with prebuilt K_bf16 (three-term split) */
+  KQ_MFMA_OTF = 2,   /* MFMA bf16 contraction, K rebuilt in-kernel from the 15 scalars */
+  KQ_BUTTERFLY = 3   /* five fp32 2x2 butterfly stages from the 15 scalars, no MFMA */
+} kq_variant;
+
+/* Front-ends of kq_transform_f32. */
+typedef enum { KQ_FRONT_KRON = 0, KQ_FRONT_PLAIN = 1, KQ_FRONT_SMOOTH = 2, KQ_FRONT_HADAMARD = 3 } kq_front;
+
+/* ABI version of this header (bumped on any signature or layout change). */
+#define KQ_ABI_VERSION 1
+int kq_abi_version(void);
+
+/* Static, never-NULL description of a status code. */
+const char* kq_status_str(kq_status status);
+
+/*
+ * Dense blocks from the 15 scalars per block (the "precomputed dense blocks"
+ * kernel variant of the review, "What carries the argument").  For each of
+ * nb blocks, with parameters at K_params + 15 j: K = G1 (x) ... (x) G5 with
+ * every entry the product, in fp64 and in factor order, of one entry of each
+ * factor (G1 on bit 4 of the row and column index, G5 on bit 0), then
+ * rounded once to fp32.  Writes K_f32 [nb][32][32] if non-NULL and the
+ * transposed bf16 split K_bf16 [nb][n_split][32][32] if non-NULL
+ * (1 <= n_split <= 3).  At least one output must be non-NULL.
+ */
+kq_status kq_build_blocks(const float* K_params, int64_t nb, float* K_f32, uint16_t* K_bf16, int n_split,
+                          hipStream_t stream);
+
+/*
+ * The online quantizer: codes and scales of X K for every block, with K
+ * built from K_params (stride 15).  Equivalent to kq_quantize_ex(X, tokens,
+ * d, K_params, 15, NULL, KQ_AUTO, out_codes, out_scales, stream).
+ */
+kq_status kq_quantize(const uint16_t* X, int64_t tokens, int64_t d, const float* K_params, uint8_t* out_codes,
+                      uint8_t* out_scales, hipStream_t stream);
+
+/*
+ * As kq_quantize, choosing how K is applied.  params_block_stride is 15 (one
+ * parameter set per block) or 0 (block 0's parameters, and K_bf16's block 0,
+ * for every block).  K_bf16 (three-term split from kq_build_blocks, layout
+ * above) is required by KQ_MFMA_DENSE and ignored by the other variants;
+ * K_params is required by every variant except KQ_MFMA_DENSE.  KQ_AUTO uses
+ * KQ_MFMA_DENSE when K_bf16 is given and K_params is NULL.
+ */
+kq_status kq_quantize_ex(const uint16_t* X, int64_t tokens, int64_t d, const float* K_params,
+                         int64_t params_block_stride, const uint16_t* K_bf16, kq_variant variant,
+                         uint8_t* out_codes, uint8_t* out_scales, hipStream_t stream);
+
+/* Plain MXFP4: y = x. */
+kq_status kq_mx_quantize(const uint16_t* X, int64_t tokens, int64_t d, uint8_t* out_codes, uint8_t* out_scales,
+                         hipStream_t stream);
+
+/*
+ * SmoothQuant front-end then MXFP4: y = fp32(x * ch_mult[c]) (one rounding),
+ * the activation side of X diag(s)^-1 with ch_mult = 1/s (SmoothQuant, the
+ * handbook page "Quantization: where diffusion differs from an LLM",
+ * SmoothQuant section; the per-channel scaling baseline of the review).
+ */
+kq_status kq_smooth_quantize(const uint16_t* X, int64_t tokens, int64_t d, const float* ch_mult,
+                             uint8_t* out_codes, uint8_t* out_scales, hipStream_t stream);
+
+/*
+ * Fixed block-Hadamard front-end then MXFP4: y[c] = fp32(sum_r x[r] H[r][c] /
+ * sqrt(32)) with H[r][c] = (-1)^popcount(r & c) (natural-order Walsh-
+ * Hadamard, orthonormal), the "fixed Hadamard at the same block size" of the
+ * review's significance paragraph.
+ */
+kq_status kq_hadamard_quantize(const uint16_t* X, int64_t tokens, int64_t d, uint8_t* out_codes,
+                               uint8_t* out_scales, hipStream_t stream);
+
+/*
+ * Diagnostic entry (tests): runs the same kernels as the entries above and
+ * also stores Y, the fp32 values each code was rounded from.  front selects
+ * the front-end; variant, K_params, params_block_stride and K_bf16 apply to
+ * KQ_FRONT_KRON as in kq_quantize_ex, ch_mult to KQ_FRONT_SMOOTH.
+ */
+kq_status kq_transform_f32(int front, const uint16_t* X, int64_t tokens, int64_t d, const float* K_params,
+                           int64_t params_block_stride, const uint16_t* K_bf16, kq_variant variant,
+                           const float* ch_mult, float* Y, uint8_t* out_codes, uint8_t* out_scales,
+                           hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KQ_H */

@@ -56,6 +56,8 @@ def lib():
         L.kqo_quantize_block.argtypes = [vp, vp, vp]
         L.kqo_quantize_rows.argtypes = [ci, vp, i64, i64, vp, i64, vp, i64, i64, vp, vp, vp, vp]
         L.kqo_quantize_rows.restype = ci
+        L.kqo_quantize_f32_rows.argtypes = [vp, i64, i64, vp, vp]
+        L.kqo_quantize_f32_rows.restype = ci
         L.kqo_fwht32.argtypes = [vp]
         L.kqo_det.argtypes = [vp, ci]
         L.kqo_det.restype = d
@@ -132,6 +134,17 @@ def quantize_block(y) -> tuple[np.ndarray, int]:
     sc = np.zeros(1, dtype=np.uint8)
     lib().kqo_quantize_block(y.ctypes.data, codes.ctypes.data, sc.ctypes.data)
     return codes, int(sc[0])
+
+
+def quantize_f32_rows(Y: np.ndarray):
+    """MXFP4 codes and scales of fp32 values Y [n, d] (no transform)."""
+    Y = np.ascontiguousarray(Y, dtype=np.float32)
+    n, d = Y.shape
+    codes = np.zeros((n, d // 2), dtype=np.uint8)
+    scales = np.zeros((n, d // 32), dtype=np.uint8)
+    if lib().kqo_quantize_f32_rows(Y.ctypes.data, n, d, codes.ctypes.data, scales.ctypes.data) != 0:
+        raise ValueError("oracle rejected its arguments")
+    return codes, scales
 
 
 def fwht32(v) -> np.ndarray:

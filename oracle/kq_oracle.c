@@ -293,3 +293,11 @@ int kqo_quantize_rows(int front, const uint16_t* X, int64_t T, int64_t d, const 
   free(K32);
   return 0;
 }
+
+int kqo_quantize_f32_rows(const float* Y, int64_t n, int64_t d, uint8_t* codes, uint8_t* scales) {
+  if (!Y || !codes || !scales || n < 0 || d <= 0 || d % 32 != 0) return 1;
+  const int64_t nb = d / 32;
+  for (int64_t t = 0; t < n; ++t)
+    for (int64_t j = 0; j < nb; ++j) kqo_quantize_block(Y + t * d + 32 * j, codes + t * (d / 2) + 16 * j, scales + t * nb + j);
+  return 0;
+}

@@ -69,6 +69,9 @@ int kqo_quantize_rows(int front, const uint16_t* X, int64_t T, int64_t d, const 
                       const float* m, int64_t row0, int64_t row1, uint8_t* codes, uint8_t* scales, float* y32,
                       double* yhat);
 
+/* MXFP4 of given fp32 values Y[n][d] (steps after the transform only). */
+int kqo_quantize_f32_rows(const float* Y, int64_t n, int64_t d, uint8_t* codes, uint8_t* scales);
+
 /* Fast Walsh-Hadamard transform of 32 values in place (natural order, unnormalized). */
 void kqo_fwht32(double v[32]);
 /* Determinant of an n x n fp64 matrix by LU with partial pivoting. */

@@ -1,0 +1,377 @@
+"""Parity of the HIP library (through its C ABI) with the CPU oracle, on an MI355X.
+
+Every case generates seeded inputs on the host, runs a libkq entry point on
+cuda:0 and compares element by element with the oracle run on the same
+inputs: E8M0 scales bit-exact, E2M1 codes exact except at rounding ties
+inside the transform's error bound (>= 99.99% exact), pre-quantization values
+within 1e-5 of the block amax, and bit-exact codes for the front-ends without
+accumulation.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle.compare import compare, transform_error
+
+kq = pytest.importorskip("w4a4_diffusion_transformer_amd")
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = {"mfma_dense": 1, "mfma_otf": 2, "butterfly": 3}
+THREADS = max(1, min(16, os.cpu_count() or 1))
+REPORT = os.environ.get("KQ_PARITY_REPORT")
+
+
+def record(name: str, rep) -> None:
+    """Append one parity line to $KQ_PARITY_REPORT (per-workload mismatch counts)."""
+    print(f"{name}: {rep}", flush=True)
+    if REPORT:
+        with open(REPORT, "a") as f:
+            f.write(f"{name}: {rep}\n")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kq.lib()
+    yield
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy()
+
+
+def build_split(Pd: torch.Tensor, nb: int) -> torch.Tensor:
+    Kbf = torch.empty((nb, 3, 32, 32), dtype=torch.int16, device="cuda:0")
+    kq.kq_build_blocks(Pd, nb, None, Kbf, 3)
+    return Kbf
+
+
+def run_kron(X: np.ndarray, P: np.ndarray, variant: str, pstride: int = 15, want_y: bool = False):
+    Xd, Pd = dev(X), dev(P)
+    codes, scales = kq.alloc_outputs(Xd)
+    Kbf = build_split(Pd, P.shape[0]) if variant == "mfma_dense" else None
+    v = VARIANTS[variant]
+    Pin = None if variant == "mfma_dense" else Pd
+    if want_y:
+        Y = torch.empty(X.shape, dtype=torch.float32, device="cuda:0")
+        kq.kq_transform_f32(kq.KQ_FRONT_KRON, Xd, Pin, pstride, Kbf, v, None, Y, codes, scales)
+        torch.cuda.synchronize()
+        return host(codes), host(scales), host(Y)
+    kq.kq_quantize_ex(Xd, Pin, pstride, Kbf, v, codes, scales)
+    torch.cuda.synchronize()
+    return host(codes), host(scales), None
+
+
+def oracle_ref(front, X, P=None, pstride=15, m=None, want_y=False):
+    return oracle.quantize_rows(front, X, P, pstride, m, want_y=want_y, threads=THREADS)
+
+
+def yhat_fn(front, X, P=None, pstride=15, m=None):
+    def f(rows):
+        o = oracle.quantize_rows(front, X[rows], P, pstride, m, want_y=True)
+        return o["yhat"], o["y32"]
+    return f
+
+
+def check_kron(X, P, variant, pstride=15, want_y=True, exact=False):
+    codes, scales, Y = run_kron(X, P, variant, pstride, want_y)
+    ref = oracle_ref(oracle.KRON, X, P, pstride, want_y=want_y)
+    rep = compare(codes, scales, ref["codes"], ref["scales"], yhat_fn(oracle.KRON, X, P, pstride))
+    assert rep.ok(exact=exact), f"{variant}: {rep}"
+    if want_y:
+        err = transform_error(Y, ref["yhat"], ref["y32"])
+        assert err <= 1e-5, f"{variant}: transform error {err:.3g} of block amax"
+        # the quantizer applied to the GPU's own y reproduces its codes and scales bit for bit
+        c2, s2 = oracle.quantize_f32_rows(Y)
+        np.testing.assert_array_equal(s2, scales)
+        np.testing.assert_array_equal(c2, codes)
+    return rep
+
+
+# ---------------------------------------------------------------- dense blocks
+
+
+def test_build_blocks_bit_exact():
+    P = synth.random_params(40, seed=21, sigma_lb=0.3, sigma_a=0.3)
+    Pd = dev(P)
+    K32 = torch.empty((40, 32, 32), dtype=torch.float32, device="cuda:0")
+    for n_split in (1, 2, 3):
+        Kbf = torch.empty((40, n_split, 32, 32), dtype=torch.int16, device="cuda:0")
+        kq.kq_build_blocks(Pd, 40, K32, Kbf, n_split)
+        torch.cuda.synchronize()
+        rK32, rKbf = oracle.build_blocks(P, 40, n_split=n_split)
+        np.testing.assert_array_equal(host(K32), rK32)
+        np.testing.assert_array_equal(host(Kbf).view(np.uint16), rKbf)
+
+
+# ---------------------------------------------------------------- tiny workload
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_tiny_config(variant):
+    spec = synth.CONFIGS[0][0]
+    check_kron(synth.matrix(spec), synth.params(spec), variant)
+
+
+def test_tiny_config_default_entry():
+    spec = synth.CONFIGS[0][0]
+    X, P = synth.matrix(spec), synth.params(spec)
+    Xd, Pd = dev(X), dev(P)
+    codes, scales = kq.alloc_outputs(Xd)
+    kq.kq_quantize(Xd, Pd, codes, scales)
+    torch.cuda.synchronize()
+    ref = oracle_ref(oracle.KRON, X, P)
+    rep = compare(host(codes), host(scales), ref["codes"], ref["scales"], yhat_fn(oracle.KRON, X, P))
+    assert rep.ok(), str(rep)
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_identity_block_equals_plain(variant):
+    """Identity factors give K = I: the KroQuant output equals plain MXFP4 bit for bit."""
+    X = synth.random_matrix(97, 1152, seed=31, n_outliers=12)
+    P = np.tile(np.array([0.0, 1.0, 0.0], dtype=np.float32), (36, 5, 1))
+    codes, scales, _ = run_kron(X, P, variant)
+    Xd = dev(X)
+    pc, ps = kq.alloc_outputs(Xd)
+    kq.kq_mx_quantize(Xd, pc, ps)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(scales, host(ps))
+    np.testing.assert_array_equal(codes, host(pc))
+
+
+# ---------------------------------------------------------------- edge shapes
+
+EDGE_SHAPES = [(1, 32), (7, 64), (33, 96), (16, 32), (17, 12288), (257, 2240), (31, 5600), (300, 1152), (1000, 160)]
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+@pytest.mark.parametrize("shape", EDGE_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+def test_edge_shapes(variant, shape):
+    T, d = shape
+    X = synth.random_matrix(T, d, seed=T * 7 + d, n_outliers=max(1, d // 100), mult=60.0)
+    P = synth.random_params(d // 32, seed=d + 3)
+    check_kron(X, P, variant)
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_shared_k_stride_zero(variant):
+    X = synth.random_matrix(200, 2240, seed=5, n_outliers=45, mult=80.0)
+    P = synth.random_params(1, seed=77)
+    check_kron(X, P, variant, pstride=0)
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_wide_parameter_spread(variant):
+    """Factors far from the identity (sigma 0.5) still meet the error bound."""
+    X = synth.random_matrix(128, 1024, seed=9, n_outliers=10)
+    P = synth.random_params(32, seed=99, sigma_lb=0.5, sigma_a=0.5)
+    check_kron(X, P, variant)
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_zero_blocks_and_zero_rows(variant):
+    X = synth.random_matrix(64, 512, seed=4)
+    X[3] = 0
+    X[10, 64:96] = 0
+    X[:, 32:64] = 0
+    P = synth.random_params(16, seed=8)
+    check_kron(X, P, variant)
+    codes, scales, _ = run_kron(X, P, variant)
+    assert np.all(scales[3] == 0) and np.all(codes[3] == 0)
+    assert np.all(scales[:, 1] == 0) and np.all(codes[:, 16:32] == 0)
+
+
+# ---------------------------------------------------------------- comparison front-ends
+
+
+def run_front(front, X, m=None, want_y=False):
+    Xd = dev(X)
+    codes, scales = kq.alloc_outputs(Xd)
+    md = None if m is None else dev(m)
+    if want_y:
+        Y = torch.empty(X.shape, dtype=torch.float32, device="cuda:0")
+        kq.kq_transform_f32(front, Xd, None, 15, None, 0, md, Y, codes, scales)
+        torch.cuda.synchronize()
+        return host(codes), host(scales), host(Y)
+    if front == kq.KQ_FRONT_PLAIN:
+        kq.kq_mx_quantize(Xd, codes, scales)
+    elif front == kq.KQ_FRONT_SMOOTH:
+        kq.kq_smooth_quantize(Xd, md, codes, scales)
+    else:
+        kq.kq_hadamard_quantize(Xd, codes, scales)
+    torch.cuda.synchronize()
+    return host(codes), host(scales), None
+
+
+ORACLE_FRONT = {0: oracle.KRON, 1: oracle.PLAIN, 2: oracle.SMOOTH, 3: oracle.HADAMARD}
+
+
+@pytest.mark.parametrize("shape", [(256, 1152), (33, 96), (1, 32), (129, 5600)], ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("front", [1, 2, 3], ids=["plain", "smooth", "hadamard"])
+def test_comparison_front_ends(front, shape):
+    T, d = shape
+    X = synth.random_matrix(T, d, seed=T + d, n_outliers=max(1, d // 80))
+    m = synth.smooth_mult(X) if front == 2 else None
+    of = ORACLE_FRONT[front]
+    ref = oracle_ref(of, X, m=m, want_y=True)
+    for want_y in (False, True):
+        codes, scales, Y = run_front(front, X, m, want_y)
+        rep = compare(codes, scales, ref["codes"], ref["scales"], yhat_fn(of, X, m=m))
+        assert rep.ok(exact=front != 3), str(rep)
+        if want_y:
+            if front == 3:
+                assert transform_error(Y, ref["yhat"], ref["y32"]) <= 1e-5
+            else:
+                np.testing.assert_array_equal(Y, ref["y32"])
+
+
+def handcrafted_rows() -> np.ndarray:
+    """Rows of bf16 values that hit every rounding rule of the quantizer exactly."""
+    f = []
+    mids = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    # midpoints at several binades with amax 6 * 2^k (scale 2^k)
+    for k in (-20, -3, 0, 5, 40):
+        row = np.zeros(64, dtype=np.float32)
+        row[0] = 6.0 * 2.0 ** k
+        row[1:8] = np.array(mids) * 2.0 ** k
+        row[8:15] = -np.array(mids) * 2.0 ** k
+        row[32] = 4.0 * 2.0 ** k  # amax exactly a power of two
+        row[33:40] = np.array(mids) * 2.0 ** (k - 1)
+        f.append(row)
+    row = np.zeros(64, dtype=np.float32)
+    row[0:32] = -1e-30  # negative tiny: every code 0x8 in its own scale
+    row[32] = 3.3e38  # near the bf16 maximum
+    row[33] = -1.0
+    f.append(row)
+    row = np.zeros(64, dtype=np.float32)
+    row[5] = 7.9
+    row[6] = 7.99
+    row[7] = -8.0
+    row[40] = 1e-39  # subnormal
+    row[41] = -2e-39
+    f.append(row)
+    f.append(np.zeros(64, dtype=np.float32))
+    X = synth.f32_to_bf16(np.stack(f))
+    X[-1, 10] = 0x8000  # -0.0
+    return X
+
+
+@pytest.mark.parametrize("front", [1, 2], ids=["plain", "smooth"])
+def test_handcrafted_exact(front):
+    X = handcrafted_rows()
+    m = np.ones(X.shape[1], dtype=np.float32) if front == 2 else None
+    if front == 2:
+        m[::3] = 0.5
+    ref = oracle_ref(ORACLE_FRONT[front], X, m=m)
+    codes, scales, _ = run_front(front, X, m)
+    np.testing.assert_array_equal(scales, ref["scales"])
+    np.testing.assert_array_equal(codes, ref["codes"])
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_handcrafted_kron_identity(variant):
+    X = handcrafted_rows()
+    X[X == 0x8000] = 0  # -0 is not a value an exact sum produces
+    P = np.tile(np.array([0.0, 1.0, 0.0], dtype=np.float32), (X.shape[1] // 32, 5, 1))
+    ref = oracle_ref(oracle.KRON, X, P)
+    codes, scales, _ = run_kron(X, P, variant)
+    np.testing.assert_array_equal(scales, ref["scales"])
+    np.testing.assert_array_equal(codes, ref["codes"])
+
+
+# ---------------------------------------------------------------- buffers, errors, determinism
+
+
+def test_guard_bands_and_determinism():
+    X = synth.random_matrix(123, 2240, seed=12, n_outliers=20)
+    P = synth.random_params(70, seed=13)
+    Xd, Pd = dev(X), dev(P)
+    G = 256
+    cbuf = torch.full((123 * 1120 + 2 * G,), 0xA5, dtype=torch.uint8, device="cuda:0")
+    sbuf = torch.full((123 * 70 + 2 * G,), 0x5A, dtype=torch.uint8, device="cuda:0")
+    outs = []
+    for variant in VARIANTS.values():
+        Kbf = build_split(Pd, 70) if variant == 1 else None
+        for rep in range(2):
+            kq.kq_quantize_ex(Xd, None if variant == 1 else Pd, 15, Kbf, variant,
+                              cbuf[G:G + 123 * 1120].data_ptr(), sbuf[G:G + 123 * 70].data_ptr())
+            torch.cuda.synchronize()
+            c, s = host(cbuf), host(sbuf)
+            assert np.all(c[:G] == 0xA5) and np.all(c[-G:] == 0xA5)
+            assert np.all(s[:G] == 0x5A) and np.all(s[-G:] == 0x5A)
+            outs.append((c[G:-G].copy(), s[G:-G].copy()))
+    for i in range(0, len(outs), 2):
+        np.testing.assert_array_equal(outs[i][0], outs[i + 1][0])
+        np.testing.assert_array_equal(outs[i][1], outs[i + 1][1])
+
+
+def test_zero_tokens_is_noop():
+    Xd = torch.zeros((0, 64), dtype=torch.int16, device="cuda:0")
+    codes = torch.full((16,), 7, dtype=torch.uint8, device="cuda:0")
+    P = torch.zeros((2, 5, 3), dtype=torch.float32, device="cuda:0")
+    assert kq.lib().kq_quantize(Xd.data_ptr(), 0, 64, P.data_ptr(), codes.data_ptr(), codes.data_ptr(), None) == 0
+    torch.cuda.synchronize()
+    assert torch.all(codes == 7)
+
+
+def test_error_codes_on_device_buffers():
+    X = torch.zeros((4, 64), dtype=torch.int16, device="cuda:0")
+    P = torch.zeros((2, 5, 3), dtype=torch.float32, device="cuda:0")
+    codes = torch.zeros(4 * 32 + 16, dtype=torch.uint8, device="cuda:0")
+    scales = torch.zeros(8, dtype=torch.uint8, device="cuda:0")
+    L = kq.lib()
+    assert L.kq_quantize(X.data_ptr() + 2, 4, 64, P.data_ptr(), codes.data_ptr(), scales.data_ptr(), None) == 3
+    assert L.kq_quantize(X.data_ptr(), 4, 64, P.data_ptr(), codes.data_ptr() + 4, scales.data_ptr(), None) == 3
+    assert L.kq_quantize(X.data_ptr(), 4, 64, P.data_ptr(), X.data_ptr(), scales.data_ptr(), None) == 6
+    assert L.kq_quantize(X.data_ptr(), 4, 48, P.data_ptr(), codes.data_ptr(), scales.data_ptr(), None) == 2
+
+
+# ---------------------------------------------------------------- full-size workloads
+
+
+FULL = [s for c in (1, 2, 3, 4) for s in synth.CONFIGS[c]]
+
+
+@pytest.mark.parametrize("spec", FULL, ids=lambda s: s.name)
+def test_full_workloads(spec):
+    """Every matrix of every workload at full size, all three variants, all rows against the oracle."""
+    X = synth.matrix(spec)
+    P = synth.params(spec)
+    pstride = 0 if spec.shared_k else 15
+    ref = oracle_ref(oracle.KRON, X, P, pstride)
+    for variant in VARIANTS:
+        codes, scales, _ = run_kron(X, P, variant, pstride)
+        rep = compare(codes, scales, ref["codes"], ref["scales"], yhat_fn(oracle.KRON, X, P, pstride))
+        record(f"{spec.name} {variant}", rep)
+        assert rep.ok(), f"{spec.name} {variant}: {rep}"
+
+
+@pytest.mark.parametrize("spec", synth.CONFIGS[3], ids=lambda s: s.name)
+def test_full_flux_comparison_front_ends(spec):
+    X = synth.matrix(spec)
+    m = synth.smooth_mult(X)
+    for front in (1, 2, 3):
+        of = ORACLE_FRONT[front]
+        ref = oracle_ref(of, X, m=m if front == 2 else None)
+        codes, scales, _ = run_front(front, X, m if front == 2 else None)
+        rep = compare(codes, scales, ref["codes"], ref["scales"], yhat_fn(of, X, m=m if front == 2 else None))
+        record(f"{spec.name} {['kron', 'plain', 'smooth', 'hadamard'][front]}", rep)
+        assert rep.ok(exact=front != 3), str(rep)
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_flux_x1_transform_error(variant):
+    spec = synth.CONFIGS[3][0].with_rows(1024)
+    check_kron(synth.matrix(spec), synth.params(spec), variant)

@@ -1,0 +1,254 @@
+// C ABI of libkq: argument checks, variant choice, launch geometry.
+// The declarations and the contract are in include/kq.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+
+#include "kq.h"
+#include "kq_device.hpp"
+#include "kq_internal.h"
+
+namespace {
+
+using kq::KSRC_PARAMS;
+using kq::KSRC_SPLIT;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+  const void* p;
+  uint64_t bytes;
+};
+
+bool overlap(const Range& a, const Range& b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+// Every output against every input and every other output.
+bool any_alias(const Range* outs, int nout, const Range* ins, int nin) {
+  for (int i = 0; i < nout; ++i) {
+    for (int k = 0; k < nin; ++k)
+      if (overlap(outs[i], ins[k])) return true;
+    for (int k = i + 1; k < nout; ++k)
+      if (overlap(outs[i], outs[k])) return true;
+  }
+  return false;
+}
+
+// Optional tuning overrides, read once: KQ_VARIANT (auto, mfma_dense, mfma_otf,
+// butterfly) and KQ_ROWS_PER_CHUNK (a positive multiple of 16).
+struct Overrides {
+  int variant = -1;
+  int rows = 0;
+};
+
+const Overrides& overrides() {
+  static const Overrides o = [] {
+    Overrides r;
+    if (const char* v = std::getenv("KQ_VARIANT")) {
+      if (!std::strcmp(v, "mfma_dense")) r.variant = KQ_MFMA_DENSE;
+      else if (!std::strcmp(v, "mfma_otf")) r.variant = KQ_MFMA_OTF;
+      else if (!std::strcmp(v, "butterfly")) r.variant = KQ_BUTTERFLY;
+    }
+    if (const char* v = std::getenv("KQ_ROWS_PER_CHUNK")) {
+      const int n = std::atoi(v);
+      if (n > 0 && n % 16 == 0) r.rows = n;
+    }
+    return r;
+  }();
+  return o;
+}
+
+// Compute units of the current device, cached per device.
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Rows per wave: enough waves to fill the machine about once (16 per CU),
+// and no fewer rows than `min_rows` so that per-wave setup stays small
+// against the streaming work.
+int rows_per_chunk(int T, int npairs, int min_rows) {
+  if (overrides().rows > 0) return overrides().rows;
+  const int64_t target_waves = (int64_t)cu_count() * 16;
+  int64_t chunks = (target_waves + npairs - 1) / npairs;
+  if (chunks < 1) chunks = 1;
+  int64_t rows = ((int64_t)T + chunks - 1) / chunks;
+  rows = (rows + 15) / 16 * 16;
+  if (rows < min_rows) rows = min_rows;
+  if (rows < 16) rows = 16;
+  return (int)rows;
+}
+
+void geometry(int T, int nb, int min_rows, int& npairs, int& rows, int& nwork) {
+  npairs = (nb + 1) / 2;
+  rows = rows_per_chunk(T, npairs, min_rows);
+  const int chunks = (T + rows - 1) / rows;
+  nwork = chunks * npairs;
+}
+
+kq_status check_shape(int64_t tokens, int64_t d) {
+  if (tokens < 0 || d <= 0 || d % 32 != 0) return KQ_ERR_SHAPE;
+  if (tokens >= (int64_t(1) << 31) || d >= (int64_t(1) << 31) || tokens * d >= (int64_t(1) << 40)) return KQ_ERR_SHAPE;
+  return KQ_OK;
+}
+
+kq_status from_hip(hipError_t e) { return e == hipSuccess ? KQ_OK : KQ_ERR_HIP; }
+
+// Shared body of every quantize entry point.
+kq_status run(int front, const uint16_t* X, int64_t tokens, int64_t d, const float* P, int64_t pstride,
+              const uint16_t* Kbf, int variant, const float* m, float* Y, uint8_t* codes, uint8_t* scales,
+              hipStream_t stream) {
+  kq_status st = check_shape(tokens, d);
+  if (st != KQ_OK) return st;
+  if (front < kq::FRONT_KRON || front > kq::FRONT_HADAMARD) return KQ_ERR_VARIANT;
+  if (variant < KQ_AUTO || variant > KQ_BUTTERFLY) return KQ_ERR_VARIANT;
+  if (front == kq::FRONT_KRON && pstride != 15 && pstride != 0) return KQ_ERR_SHAPE;
+  if (tokens == 0) return KQ_OK;
+  if (!X || !codes || !scales) return KQ_ERR_NULL;
+  if (front == kq::FRONT_SMOOTH && !m) return KQ_ERR_NULL;
+  if (front == kq::FRONT_KRON) {
+    if (variant == KQ_AUTO) {
+      if (overrides().variant > 0 && (overrides().variant != KQ_MFMA_DENSE || Kbf)) variant = overrides().variant;
+      else if (!P && Kbf) variant = KQ_MFMA_DENSE;
+      else variant = KQ_MFMA_OTF;
+    }
+    if (variant == KQ_MFMA_DENSE && !Kbf) return KQ_ERR_VARIANT;
+    if (variant != KQ_MFMA_DENSE && !P) return KQ_ERR_VARIANT;
+  }
+  if (!aligned(X, 16) || !aligned(codes, 16) || (Y && !aligned(Y, 16))) return KQ_ERR_ALIGN;
+  if (P && !aligned(P, 4)) return KQ_ERR_ALIGN;
+  if (Kbf && !aligned(Kbf, 16)) return KQ_ERR_ALIGN;
+  if (m && !aligned(m, 16)) return KQ_ERR_ALIGN;
+
+  const int64_t nb = d / 32;
+  const uint64_t n = (uint64_t)tokens * (uint64_t)d;
+  const uint64_t nk = pstride == 0 ? 1 : (uint64_t)nb;
+  const Range outs[] = {{codes, n / 2}, {scales, n / 32}, {Y, Y ? n * 4 : 0}};
+  const Range ins[] = {{X, n * 2},
+                       {front == kq::FRONT_KRON ? P : nullptr, nk * 60},
+                       {front == kq::FRONT_KRON && variant == KQ_MFMA_DENSE ? Kbf : nullptr, nk * 3 * 2048},
+                       {front == kq::FRONT_SMOOTH ? m : nullptr, (uint64_t)d * 4}};
+  if (any_alias(outs, 3, ins, 4)) return KQ_ERR_ALIAS;
+
+  const int T = (int)tokens;
+  if (front == kq::FRONT_KRON && variant != KQ_BUTTERFLY) {
+    kq::MfmaArgs a{};
+    a.X = X;
+    a.T = T;
+    a.d = (int)d;
+    a.nb = (int)nb;
+    a.P = P;
+    a.pstride = (int)pstride;
+    a.Kbf = Kbf;
+    a.kstride = pstride == 0 ? 0 : 3 * 1024;
+    a.codes = codes;
+    a.scales = scales;
+    a.Y = Y;
+    geometry(T, a.nb, variant == KQ_MFMA_OTF ? 64 : 32, a.npairs, a.rows_per_chunk, a.nwork);
+    return from_hip(kq::launch_mfma(variant == KQ_MFMA_OTF ? KSRC_PARAMS : KSRC_SPLIT, Y != nullptr, a, stream));
+  }
+  kq::QuadArgs a{};
+  a.X = X;
+  a.T = T;
+  a.d = (int)d;
+  a.nb = (int)nb;
+  a.P = P;
+  a.pstride = (int)pstride;
+  a.m = m;
+  a.codes = codes;
+  a.scales = scales;
+  a.Y = Y;
+  geometry(T, a.nb, front == kq::FRONT_KRON ? 64 : 32, a.npairs, a.rows_per_chunk, a.nwork);
+  return from_hip(kq::launch_quad(front, Y != nullptr, a, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int kq_abi_version(void) { return KQ_ABI_VERSION; }
+
+const char* kq_status_str(kq_status s) {
+  switch (s) {
+    case KQ_OK: return "ok";
+    case KQ_ERR_NULL: return "null pointer argument";
+    case KQ_ERR_SHAPE: return "invalid shape or stride";
+    case KQ_ERR_ALIGN: return "misaligned pointer";
+    case KQ_ERR_VARIANT: return "invalid variant or missing variant input";
+    case KQ_ERR_HIP: return "HIP launch failure";
+    case KQ_ERR_ALIAS: return "output overlaps an input or another output";
+  }
+  return "unknown status";
+}
+
+kq_status kq_build_blocks(const float* K_params, int64_t nb, float* K_f32, uint16_t* K_bf16, int n_split,
+                          hipStream_t stream) {
+  if (nb <= 0 || nb >= (int64_t(1) << 20)) return KQ_ERR_SHAPE;
+  if (K_bf16 && (n_split < 1 || n_split > 3)) return KQ_ERR_SHAPE;
+  if (!K_params || (!K_f32 && !K_bf16)) return KQ_ERR_NULL;
+  if (!aligned(K_params, 4) || (K_f32 && !aligned(K_f32, 4)) || (K_bf16 && !aligned(K_bf16, 16)))
+    return KQ_ERR_ALIGN;
+  const uint64_t n = (uint64_t)nb;
+  const Range outs[] = {{K_f32, n * 4096}, {K_bf16, K_bf16 ? n * 2048 * (uint64_t)n_split : 0}};
+  const Range ins[] = {{K_params, n * 60}};
+  if (any_alias(outs, 2, ins, 1)) return KQ_ERR_ALIAS;
+  return from_hip(kq::launch_build(K_params, (int)nb, K_f32, K_bf16, K_bf16 ? n_split : 0, stream));
+}
+
+kq_status kq_quantize(const uint16_t* X, int64_t tokens, int64_t d, const float* K_params, uint8_t* out_codes,
+                      uint8_t* out_scales, hipStream_t stream) {
+  if (tokens > 0 && !K_params) return KQ_ERR_NULL;
+  return run(kq::FRONT_KRON, X, tokens, d, K_params, 15, nullptr, KQ_AUTO, nullptr, nullptr, out_codes,
+             out_scales, stream);
+}
+
+kq_status kq_quantize_ex(const uint16_t* X, int64_t tokens, int64_t d, const float* K_params,
+                         int64_t params_block_stride, const uint16_t* K_bf16, kq_variant variant,
+                         uint8_t* out_codes, uint8_t* out_scales, hipStream_t stream) {
+  return run(kq::FRONT_KRON, X, tokens, d, K_params, params_block_stride, K_bf16, (int)variant, nullptr,
+             nullptr, out_codes, out_scales, stream);
+}
+
+kq_status kq_mx_quantize(const uint16_t* X, int64_t tokens, int64_t d, uint8_t* out_codes, uint8_t* out_scales,
+                         hipStream_t stream) {
+  return run(kq::FRONT_PLAIN, X, tokens, d, nullptr, 15, nullptr, KQ_AUTO, nullptr, nullptr, out_codes,
+             out_scales, stream);
+}
+
+kq_status kq_smooth_quantize(const uint16_t* X, int64_t tokens, int64_t d, const float* ch_mult,
+                             uint8_t* out_codes, uint8_t* out_scales, hipStream_t stream) {
+  return run(kq::FRONT_SMOOTH, X, tokens, d, nullptr, 15, nullptr, KQ_AUTO, ch_mult, nullptr, out_codes,
+             out_scales, stream);
+}
+
+kq_status kq_hadamard_quantize(const uint16_t* X, int64_t tokens, int64_t d, uint8_t* out_codes,
+                               uint8_t* out_scales, hipStream_t stream) {
+  return run(kq::FRONT_HADAMARD, X, tokens, d, nullptr, 15, nullptr, KQ_AUTO, nullptr, nullptr, out_codes,
+             out_scales, stream);
+}
+
+kq_status kq_transform_f32(int front, const uint16_t* X, int64_t tokens, int64_t d, const float* K_params,
+                           int64_t params_block_stride, const uint16_t* K_bf16, kq_variant variant,
+                           const float* ch_mult, float* Y, uint8_t* out_codes, uint8_t* out_scales,
+                           hipStream_t stream) {
+  if (tokens > 0 && !Y) {
+    if (check_shape(tokens, d) != KQ_OK) return KQ_ERR_SHAPE;
+    return KQ_ERR_NULL;
+  }
+  return run(front, X, tokens, d, K_params, params_block_stride, K_bf16, (int)variant, ch_mult, Y, out_codes,
+             out_scales, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,223 @@
+// Device-side building blocks shared by the libkq kernels (gfx950 only).
+//
+// Every kernel maps one 32-channel block of one token onto a group of four
+// lanes; each lane owns 8 consecutive channels (8q .. 8q+7, q = 0..3) of the
+// block.  Two lane layouts exist:
+//   LAYOUT_MFMA  the lane order of a 16x16x32 MFMA result: lanes l, l^16,
+//                l^32, l^48 share a token (q = lane >> 4);
+//   LAYOUT_QUAD  four adjacent lanes share a token (q = lane & 3).
+// The MXFP4 epilogue (block amax, E8M0 byte, E2M1 codes) is the same for
+// both, only the cross-lane reduction differs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kq {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+
+enum { FRONT_KRON = 0, FRONT_PLAIN = 1, FRONT_SMOOTH = 2, FRONT_HADAMARD = 3 };
+enum { LAYOUT_MFMA = 0, LAYOUT_QUAD = 1 };
+
+// Half-width of the window around a power of two inside which a block's
+// scale is decided by exact arithmetic: 2^-16 relative, above the transform's
+// worst-case fp32 error (1e-5 of the block amax) with margin.
+constexpr unsigned kNearLoMant = 1u << 7;              // amax in [2^n, 2^n (1 + 2^-16))
+constexpr unsigned kNearHiMant = (1u << 23) - (1u << 8);  // amax in [2^(n+1) (1 - 2^-16), 2^(n+1))
+
+__device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+// ---------------------------------------------------------------- factors
+
+// One Kronecker factor in fp64: G = [[1,0],[l,1]] [[a,b],[0,1/a]]
+// = [[a, b], [l a, l b + 1/a]] (KroQuant, Sec. 3.2 Eq. (6) as the Pith review
+// quotes it, with the determinant +1 form of U).  l a and l b are exact in
+// fp64; 1/a and the final sum are single correctly rounded operations.
+__device__ __forceinline__ void factor_f64(const float* p, double G[4]) {
+  const double L = p[0], A = p[1], B = p[2];
+  const double inv_a = 1.0 / A;
+  G[0] = A;
+  G[1] = B;
+  G[2] = L * A;
+  G[3] = L * B + inv_a;
+}
+
+__device__ __forceinline__ void factors_f64(const float* __restrict__ p15, double G[5][4]) {
+#pragma unroll
+  for (int k = 0; k < 5; ++k) factor_f64(p15 + 3 * k, G[k]);
+}
+
+// K[r][c] of K = G1 (x) ... (x) G5 (G1 on bit 4 of r and c, G5 on bit 0): the
+// product of one entry per factor, multiplied in factor order in fp64, then
+// rounded once to fp32.
+__device__ __forceinline__ float k32_entry(const double G[5][4], int r, int c) {
+  double p = G[0][2 * ((r >> 4) & 1) + ((c >> 4) & 1)];
+#pragma unroll
+  for (int k = 1; k < 5; ++k) p = p * G[k][2 * ((r >> (4 - k)) & 1) + ((c >> (4 - k)) & 1)];
+  return (float)p;
+}
+
+// ---------------------------------------------------------------- cross-lane
+
+__device__ __forceinline__ float dpp_quad_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_quad_xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+
+// Maximum over the four lanes that hold one token's block (v >= 0).
+template <int LAYOUT>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (LAYOUT == LAYOUT_QUAD) {
+    v = fmaxf(v, dpp_quad_xor1(v));
+    v = fmaxf(v, dpp_quad_xor2(v));
+    return v;
+  } else {
+    unsigned u = __float_as_uint(v);
+    auto s16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // lanes l and l^16
+    v = fmaxf(v, fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1])));
+    u = __float_as_uint(v);
+    auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);  // lanes l and l^32
+    return fmaxf(v, fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1])));
+  }
+}
+
+__device__ __forceinline__ float local_absmax8(const float y[8]) {
+  float a = fmaxf(fabsf(y[0]), fabsf(y[1]));
+  a = fmaxf(a, fmaxf(fabsf(y[2]), fabsf(y[3])));
+  a = fmaxf(a, fmaxf(fabsf(y[4]), fabsf(y[5])));
+  return fmaxf(a, fmaxf(fabsf(y[6]), fabsf(y[7])));
+}
+
+// ---------------------------------------------------------------- exact columns
+
+// Exact value of output channel c of one block, as a correctly rounded fp32:
+// the fp64 sum, from +0 in input order r = 0..31, of the exact products
+// x[r] K[r][c] (bf16 times fp32 is exact in fp64), rounded once.  K comes
+// from the 15 scalars.
+struct ExactFromParams {
+  const float* p15;
+  __device__ float operator()(const uint16_t* __restrict__ xblk, int c) const {
+    double G[5][4];
+    factors_f64(p15, G);
+    double s = 0.0;
+    for (int r = 0; r < 32; ++r) {
+      const double x = (double)__uint_as_float((unsigned)xblk[r] << 16);
+      s = fma(x, (double)k32_entry(G, r, c), s);
+    }
+    return (float)s;
+  }
+};
+
+// Same, with K read back from the three-term bf16 split [3][32 c][32 r]:
+// (hi + mid) + lo is the fp32 K exactly.
+struct ExactFromSplit {
+  const uint16_t* kblk;  // this block's [3][32][32]
+  __device__ float operator()(const uint16_t* __restrict__ xblk, int c) const {
+    double s = 0.0;
+    for (int r = 0; r < 32; ++r) {
+      const float hi = __uint_as_float((unsigned)kblk[(0 * 32 + c) * 32 + r] << 16);
+      const float mid = __uint_as_float((unsigned)kblk[(1 * 32 + c) * 32 + r] << 16);
+      const float lo = __uint_as_float((unsigned)kblk[(2 * 32 + c) * 32 + r] << 16);
+      const float k = (hi + mid) + lo;
+      const double x = (double)__uint_as_float((unsigned)xblk[r] << 16);
+      s = fma(x, (double)k, s);
+    }
+    return (float)s;
+  }
+};
+
+// Block-Hadamard column: (sum_r (-1)^popcount(r & c) x[r]) / sqrt(32) in
+// fp64 (sum from +0 in input order), rounded once to fp32.
+struct ExactHadamard {
+  __device__ float operator()(const uint16_t* __restrict__ xblk, int c) const {
+    double s = 0.0;
+    for (int r = 0; r < 32; ++r) {
+      const double x = (double)__uint_as_float((unsigned)xblk[r] << 16);
+      s = s + ((__popc(r & c) & 1) ? -x : x);
+    }
+    return (float)(s / 5.6568542494923801952067548968387923142786875015078);
+  }
+};
+
+// ---------------------------------------------------------------- epilogue
+
+// MXFP4 for one lane's 8 values of a block whose four lanes hold one token.
+// Returns the four packed code bytes (channels 8q+2k in the low nibble of
+// byte k) and the block's E8M0 byte.
+//
+//   amax  = max |y| over the 32 values (group reduction);
+//   byte  = max(exponent_field(amax) - 2, 0): floor(log2 amax) - 2 + 127,
+//           clamped at 0 (amax = 0 and subnormal amax give 0; finite fp32
+//           never reaches the upper clamp);
+//   codes = E2M1(y / 2^(byte - 127)), round to nearest even, saturating
+//           (the gfx950 scaled fp4 convert divides by the scale's power of
+//           two; it rounds exactly like the E2M1 rule above for every finite
+//           fp32 input).
+//
+// TRANSFORM front-ends (sums of products) first settle blocks whose amax is
+// within 2^-16 of a power of two: the columns that could cross it are
+// recomputed exactly by `exact`, so the scale equals the exact evaluation's.
+// An all-zero block of a transform yields +0 codes (the exact sum of zeros is
+// +0).
+template <int LAYOUT, bool TRANSFORM, class Exact>
+__device__ __forceinline__ void mx_epilogue(float y[8], const uint16_t* __restrict__ xblk, int q,
+                                            const Exact& exact, unsigned& word, unsigned& byte) {
+  float amax = group_max<LAYOUT>(local_absmax8(y));
+  if constexpr (TRANSFORM) {
+    const unsigned ab = __float_as_uint(amax);
+    const unsigned ex = ab >> 23, mant = ab & 0x7FFFFFu;
+    const bool near = ex >= 2u && (mant < kNearLoMant || mant >= kNearHiMant);
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(near) != 0, 0)) {
+      if (near) {
+        // the power of two being straddled, and the smallest |y| that could reach it
+        const unsigned pe = mant < kNearLoMant ? ex : ex + 1u;
+        const float thr = __uint_as_float(pe << 23) * (1.0f - 0x1p-14f);
+        for (int i = 0; i < 8; ++i)
+          if (fabsf(y[i]) >= thr) y[i] = exact(xblk, 8 * q + i);
+      }
+      amax = group_max<LAYOUT>(local_absmax8(y));
+    }
+  }
+  const unsigned ex = __float_as_uint(amax) >> 23;
+  byte = ex > 2u ? ex - 2u : 0u;
+  float scale;
+  if (byte != 0u) {
+    scale = __uint_as_float(byte << 23);  // 2^(byte - 127), a normal float for byte >= 1
+  } else {
+    // 2^-127 is not a normal float: scale by 2^127 exactly instead (|y| < 2^-124 here)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] *= 0x1p127f;
+    scale = 1.0f;
+  }
+  unsigned w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], scale, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], scale, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], scale, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], scale, 3);
+  if constexpr (TRANSFORM) {
+    if (amax == 0.0f) w = 0u;
+  }
+  word = w;
+  if (byte == 0u) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] *= 0x1p-127f;  // restore y for an optional diagnostic store
+  }
+}
+
+// ---------------------------------------------------------------- scheduling
+
+// Workgroups are handed to the 8 XCDs round-robin.  Renumber them so that
+// consecutive logical workgroups (adjacent columns of the same rows, which
+// share output cache lines) run on the same XCD and its L2.
+__device__ __forceinline__ int xcd_remap(int b, int G) {
+  const int per = G >> 3, rem = G & 7, x = b & 7;
+  return x * per + (x < rem ? x : rem) + (b >> 3);
+}
+
+}  // namespace kq
