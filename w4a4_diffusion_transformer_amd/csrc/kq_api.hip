@@ -5,6 +5,7 @@
 #include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "kq.h"
 #include "kq_device.hpp"
@@ -40,10 +41,10 @@ bool any_alias(const Range* outs, int nout, const Range* ins, int nin) {
 }
 
 // Optional tuning overrides, read once: KQ_VARIANT (auto, mfma_dense, mfma_otf,
-// butterfly) and KQ_ROWS_PER_CHUNK (a positive multiple of 16).
+// butterfly) and KQ_WG_PER_CU (target resident workgroups per compute unit).
 struct Overrides {
   int variant = -1;
-  int rows = 0;
+  int wg_per_cu = 0;
 };
 
 const Overrides& overrides() {
@@ -54,48 +55,13 @@ const Overrides& overrides() {
       else if (!std::strcmp(v, "mfma_otf")) r.variant = KQ_MFMA_OTF;
       else if (!std::strcmp(v, "butterfly")) r.variant = KQ_BUTTERFLY;
     }
-    if (const char* v = std::getenv("KQ_ROWS_PER_CHUNK")) {
+    if (const char* v = std::getenv("KQ_WG_PER_CU")) {
       const int n = std::atoi(v);
-      if (n > 0 && n % 16 == 0) r.rows = n;
+      if (n > 0 && n <= 64) r.wg_per_cu = n;
     }
     return r;
   }();
   return o;
-}
-
-// Compute units of the current device, cached per device.
-int cu_count() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int v = cache[dev].load(std::memory_order_relaxed);
-  if (v > 0) return v;
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-  cache[dev].store(n, std::memory_order_relaxed);
-  return n;
-}
-
-// Rows per wave: enough waves to fill the machine about once (16 per CU),
-// and no fewer rows than `min_rows` so that per-wave setup stays small
-// against the streaming work.
-int rows_per_chunk(int T, int npairs, int min_rows) {
-  if (overrides().rows > 0) return overrides().rows;
-  const int64_t target_waves = (int64_t)cu_count() * 16;
-  int64_t chunks = (target_waves + npairs - 1) / npairs;
-  if (chunks < 1) chunks = 1;
-  int64_t rows = ((int64_t)T + chunks - 1) / chunks;
-  rows = (rows + 15) / 16 * 16;
-  if (rows < min_rows) rows = min_rows;
-  if (rows < 16) rows = 16;
-  return (int)rows;
-}
-
-void geometry(int T, int nb, int min_rows, int& npairs, int& rows, int& nwork) {
-  npairs = (nb + 1) / 2;
-  rows = rows_per_chunk(T, npairs, min_rows);
-  const int chunks = (T + rows - 1) / rows;
-  nwork = chunks * npairs;
 }
 
 kq_status check_shape(int64_t tokens, int64_t d) {
@@ -156,7 +122,6 @@ kq_status run(int front, const uint16_t* X, int64_t tokens, int64_t d, const flo
     a.codes = codes;
     a.scales = scales;
     a.Y = Y;
-    geometry(T, a.nb, variant == KQ_MFMA_OTF ? 64 : 32, a.npairs, a.rows_per_chunk, a.nwork);
     return from_hip(kq::launch_mfma(variant == KQ_MFMA_OTF ? KSRC_PARAMS : KSRC_SPLIT, Y != nullptr, a, stream));
   }
   kq::QuadArgs a{};
@@ -170,11 +135,60 @@ kq_status run(int front, const uint16_t* X, int64_t tokens, int64_t d, const flo
   a.codes = codes;
   a.scales = scales;
   a.Y = Y;
-  geometry(T, a.nb, front == kq::FRONT_KRON ? 64 : 32, a.npairs, a.rows_per_chunk, a.nwork);
   return from_hip(kq::launch_quad(front, Y != nullptr, a, stream));
 }
 
 }  // namespace
+
+namespace kq {
+
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+int resident_per_cu(const void* fn, int block_threads) {
+  struct Entry {
+    const void* fn;
+    int dev, threads, value;
+  };
+  static std::mutex mu;
+  static Entry table[64];
+  static int used = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  int value = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used; ++i)
+      if (table[i].fn == fn && table[i].dev == dev && table[i].threads == block_threads) value = table[i].value;
+    if (value == 0) {
+      int n = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, block_threads, 0) != hipSuccess || n <= 0) n = 1;
+      value = n;
+      if (used < 64) table[used++] = Entry{fn, dev, block_threads, value};
+    }
+  }
+  const int cap = overrides().wg_per_cu;
+  return cap > 0 && cap < value ? cap : value;
+}
+
+int chunks_one_round(const void* fn, int block_threads, int ngroups, int ntiles) {
+  const int64_t slots = (int64_t)cu_count() * resident_per_cu(fn, block_threads);
+  int64_t ch = slots / ngroups;
+  if (ch > ntiles) ch = ntiles;
+  if (ch < 1) ch = 1;
+  return (int)ch;
+}
+
+}  // namespace kq
 
 extern "C" {
 

@@ -8,8 +8,10 @@ namespace kq {
 
 enum { KSRC_PARAMS = 0, KSRC_SPLIT = 1 };
 
-// Shared work decomposition: a wave owns blocks (2 pair, 2 pair + 1) and rows
-// [chunk * rows_per_chunk, ...); work item w = chunk * npairs + pair.
+// Tile decomposition of the MFMA kernels: a workgroup of four waves owns a
+// column group of 8 blocks (512 B of each bf16 row; each wave two blocks,
+// whose K operands stay in its registers) and processes tiles of 16 rows:
+// workgroup (group g, chunk c) takes row tiles c, c + nchunks, ...
 struct MfmaArgs {
   const uint16_t* X;
   int T, d, nb;
@@ -20,9 +22,15 @@ struct MfmaArgs {
   uint8_t* codes;
   uint8_t* scales;
   float* Y;  // diagnostic output or nullptr
-  int npairs, rows_per_chunk, nwork;
+  int ngroups, nchunks;
 };
 
+// Row-segment decomposition of the vector-ALU kernels: a workgroup of four
+// waves owns a column group of 16 blocks (1 KB of each bf16 row); each lane
+// owns one fixed 16-byte piece (8 channels) of it, so every wave instruction
+// reads 1 KB and writes 256 code bytes and 16 scale bytes, all contiguous.
+// Rows go in blocks of four (one per wave); workgroup (group g, chunk c)
+// takes row blocks c, c + nchunks, c + 2 nchunks, ...
 struct QuadArgs {
   const uint16_t* X;
   int T, d, nb;
@@ -32,8 +40,18 @@ struct QuadArgs {
   uint8_t* codes;
   uint8_t* scales;
   float* Y;
-  int npairs, rows_per_chunk, nwork;
+  int ngroups, nchunks;
 };
+
+// Compute units of the current device (cached per device).
+int cu_count();
+// Workgroups of `fn` (block_threads threads, no dynamic LDS) resident per
+// compute unit, from the occupancy calculator, cached per kernel and device;
+// capped by the KQ_WG_PER_CU tuning override when set.
+int resident_per_cu(const void* fn, int block_threads);
+// Row chunks so that ngroups x nchunks workgroups fill the machine exactly
+// once (no second, partial round), with at least one row tile per chunk.
+int chunks_one_round(const void* fn, int block_threads, int ngroups, int ntiles);
 
 hipError_t launch_mfma(int ksrc, bool store_y, const MfmaArgs& args, hipStream_t stream);
 hipError_t launch_quad(int front, bool store_y, const QuadArgs& args, hipStream_t stream);

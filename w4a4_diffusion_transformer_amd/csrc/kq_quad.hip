@@ -8,12 +8,14 @@
 //   FRONT_SMOOTH    y = x * m[c] (SmoothQuant per-channel scale);
 //   FRONT_HADAMARD  y = (x H32)[c] / sqrt(32), fast Walsh-Hadamard butterflies.
 //
-// Lane layout: four adjacent lanes hold one token's 32-channel block, lane
-// q = l & 3 owning channels 8q .. 8q+7, so a wave's 16-byte loads cover 16
-// rows x 64 contiguous bytes per block.  Stages on channel bits 0-2 stay in
-// registers; bits 3 and 4 pair lane l with l^1 and l^2, exchanged with DPP
-// quad permutes.  A wave owns two adjacent blocks and streams rows, 16
-// tokens per step, loads kept two steps ahead.
+// Lane layout: a wave covers 1 KB of one bf16 row (16 blocks); lane l owns
+// the fixed 16-byte piece l, i.e. channels 8q .. 8q+7 (q = l & 3) of block
+// l >> 2 of its column group, for every row it visits.  Loads (1 KB), code
+// stores (256 B) and scale stores (16 B) of a wave instruction are therefore
+// contiguous, and each lane keeps the coefficients of a single block in
+// registers.  Stages on channel bits 0-2 stay in registers; bits 3 and 4
+// pair lane l with l^1 and l^2 (the four lanes of a block), exchanged with
+// DPP quad permutes.  Rows stream with loads kept several rows ahead.
 #include "kq_device.hpp"
 #include "kq_internal.h"
 
@@ -21,8 +23,8 @@ namespace kq {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kDepth = 3;
+constexpr int kWaves = 4;  // waves per workgroup, one row each per step
+constexpr int kDepth = 6;  // rows in flight per wave (current + 5 ahead)
 
 // Per-lane coefficients of one block for the butterfly front-end.
 struct Coef {
@@ -106,115 +108,94 @@ template <int FRONT, bool STORE_Y>
 __global__ __launch_bounds__(64 * kWaves) void quad_kernel(QuadArgs a) {
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  const int w = xcd_remap(blockIdx.x, gridDim.x) * kWaves + wv;
-  if (w >= a.nwork) return;
-  const int pair = w % a.npairs, chunk = w / a.npairs;
-  const int j0 = 2 * pair;
-  const bool has1 = j0 + 1 < a.nb;
-  const int t_begin = chunk * a.rows_per_chunk;
-  const int t_end = min(a.T, t_begin + a.rows_per_chunk);
-  const int ntiles = (t_end - t_begin + 15) >> 4;
-  const int tl = lane >> 2, q = lane & 3;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int g = wg % a.ngroups, c = wg / a.ngroups;
+  const int j = 16 * g + (lane >> 2), q = lane & 3;
+  const bool live = j < a.nb;  // the last column group may be partial
+  const int jc = live ? j : a.nb - 1;
 
-  Coef cf[2];
-  float mult[2][8];
-  if constexpr (FRONT == FRONT_KRON) {
-    setup_coef(cf[0], a.P + (int64_t)j0 * a.pstride, q);
-    if (has1) setup_coef(cf[1], a.P + (int64_t)(j0 + 1) * a.pstride, q);
-  }
+  Coef cf;
+  float mult[8];
+  if constexpr (FRONT == FRONT_KRON) setup_coef(cf, a.P + (int64_t)jc * a.pstride, q);
   if constexpr (FRONT == FRONT_SMOOTH) {
+    const f32x4* mp = reinterpret_cast<const f32x4*>(a.m + 32 * jc + 8 * q);
+    const f32x4 m0 = mp[0], m1 = mp[1];
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      if (bb == 1 && !has1) break;
-      const f32x4* mp = reinterpret_cast<const f32x4*>(a.m + 32 * (j0 + bb) + 8 * q);
-      const f32x4 m0 = mp[0], m1 = mp[1];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        mult[bb][i] = m0[i];
-        mult[bb][4 + i] = m1[i];
-      }
+    for (int i = 0; i < 4; ++i) {
+      mult[i] = m0[i];
+      mult[4 + i] = m1[i];
     }
   }
   const float sgn3 = (q & 1) ? -1.0f : 1.0f, sgn4 = (q >> 1) ? -1.0f : 1.0f;
   constexpr float kInvSqrt32 = 0.17677669529663688110f;
 
   const int64_t d = a.d;
-  const uint16_t* xbase = a.X + 32 * j0 + 8 * q;
-  u32x4 buf[kDepth][2];
+  const int nrb = (a.T + kWaves - 1) / kWaves;  // row blocks of kWaves rows
+  const int nsteps = c < nrb ? (nrb - 1 - c) / a.nchunks + 1 : 0;
+  const uint16_t* xcol = a.X + 32 * jc + 8 * q;
+  auto row_of = [&](int s) { return kWaves * (c + s * a.nchunks) + wv; };
+  u32x4 buf[kDepth];
 
-  auto load = [&](int tile, u32x4 (&b)[2]) {
-    const int t = t_begin + 16 * tile + tl;
-    if (t < t_end) {
-      const uint16_t* p = xbase + (int64_t)t * d;
-      b[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-      b[1] = has1 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p + 32)) : u32x4{0, 0, 0, 0};
-    } else {
-      b[0] = u32x4{0, 0, 0, 0};
-      b[1] = u32x4{0, 0, 0, 0};
-    }
+  auto load = [&](int s, u32x4& b) {
+    const int r = row_of(s);
+    b = (r < a.T && live) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xcol + (int64_t)r * d))
+                          : u32x4{0, 0, 0, 0};
   };
 
-  auto compute = [&](int tile, const u32x4 (&b)[2]) {
-    const int t = t_begin + 16 * tile + tl;
-    const bool valid = t < t_end;
-    const int tc = valid ? t : t_begin;
+  auto compute = [&](int s, const u32x4& b) {
+    const int r = row_of(s);
+    if (r >= a.T) return;  // wave-uniform: one row per wave
+    float y[8];
+    unpack8(b, y);
+    if constexpr (FRONT == FRONT_KRON) {
+      stage_in_reg<1>(y, cf.g[0]);
+      stage_in_reg<2>(y, cf.g[1]);
+      stage_in_reg<4>(y, cf.g[2]);
+      stage_cross<1>(y, cf.cs[0], cf.cp[0]);
+      stage_cross<2>(y, cf.cs[1], cf.cp[1]);
+    } else if constexpr (FRONT == FRONT_SMOOTH) {
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      if (bb == 1 && !has1) break;
-      const int j = j0 + bb;
-      float y[8];
-      unpack8(b[bb], y);
-      if constexpr (FRONT == FRONT_KRON) {
-        stage_in_reg<1>(y, cf[bb].g[0]);
-        stage_in_reg<2>(y, cf[bb].g[1]);
-        stage_in_reg<4>(y, cf[bb].g[2]);
-        stage_cross<1>(y, cf[bb].cs[0], cf[bb].cp[0]);
-        stage_cross<2>(y, cf[bb].cs[1], cf[bb].cp[1]);
-      } else if constexpr (FRONT == FRONT_SMOOTH) {
+      for (int i = 0; i < 8; ++i) y[i] *= mult[i];
+    } else if constexpr (FRONT == FRONT_HADAMARD) {
+      wht_in_reg<1>(y);
+      wht_in_reg<2>(y);
+      wht_in_reg<4>(y);
+      wht_cross<1>(y, sgn3);
+      wht_cross<2>(y, sgn4);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) y[i] *= mult[bb][i];
-      } else if constexpr (FRONT == FRONT_HADAMARD) {
-        wht_in_reg<1>(y);
-        wht_in_reg<2>(y);
-        wht_in_reg<4>(y);
-        wht_cross<1>(y, sgn3);
-        wht_cross<2>(y, sgn4);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) y[i] *= kInvSqrt32;
-      }
-      const uint16_t* xblk = a.X + (int64_t)tc * d + 32 * j;
-      unsigned word, byte;
-      if constexpr (FRONT == FRONT_KRON) {
-        mx_epilogue<LAYOUT_QUAD, true>(y, xblk, q, ExactFromParams{a.P + (int64_t)j * a.pstride}, word, byte);
-      } else if constexpr (FRONT == FRONT_HADAMARD) {
-        mx_epilogue<LAYOUT_QUAD, true>(y, xblk, q, ExactHadamard{}, word, byte);
-      } else {
-        mx_epilogue<LAYOUT_QUAD, false>(y, xblk, q, NoExact{}, word, byte);
-      }
-      if (valid) {
-        uint8_t* crow = a.codes + (int64_t)t * (d >> 1);
-        *reinterpret_cast<unsigned*>(crow + 16 * j + 4 * q) = word;
-        if (q == bb) a.scales[(int64_t)t * a.nb + j] = (uint8_t)byte;
-        if constexpr (STORE_Y) {
-          float* yr = a.Y + (int64_t)t * d + 32 * j + 8 * q;
-          *reinterpret_cast<f32x4*>(yr) = f32x4{y[0], y[1], y[2], y[3]};
-          *reinterpret_cast<f32x4*>(yr + 4) = f32x4{y[4], y[5], y[6], y[7]};
-        }
+      for (int i = 0; i < 8; ++i) y[i] *= kInvSqrt32;
+    }
+    const uint16_t* xblk = a.X + (int64_t)r * d + 32 * jc;
+    unsigned word, byte;
+    if constexpr (FRONT == FRONT_KRON) {
+      mx_epilogue<LAYOUT_QUAD, true>(y, xblk, q, ExactFromParams{a.P + (int64_t)jc * a.pstride}, word, byte);
+    } else if constexpr (FRONT == FRONT_HADAMARD) {
+      mx_epilogue<LAYOUT_QUAD, true>(y, xblk, q, ExactHadamard{}, word, byte);
+    } else {
+      mx_epilogue<LAYOUT_QUAD, false>(y, xblk, q, NoExact{}, word, byte);
+    }
+    if (live) {
+      *reinterpret_cast<unsigned*>(a.codes + (int64_t)r * (d >> 1) + 16 * j + 4 * q) = word;
+      if (q == 0) a.scales[(int64_t)r * a.nb + j] = (uint8_t)byte;
+      if constexpr (STORE_Y) {
+        float* yr = a.Y + (int64_t)r * d + 32 * j + 8 * q;
+        *reinterpret_cast<f32x4*>(yr) = f32x4{y[0], y[1], y[2], y[3]};
+        *reinterpret_cast<f32x4*>(yr + 4) = f32x4{y[4], y[5], y[6], y[7]};
       }
     }
   };
 
 #pragma unroll
   for (int k = 0; k < kDepth - 1; ++k)
-    if (k < ntiles) load(k, buf[k]);
-  for (int it = 0; it < ntiles; it += kDepth) {
+    if (k < nsteps) load(k, buf[k]);
+  for (int it = 0; it < nsteps; it += kDepth) {
 #pragma unroll
     for (int k = 0; k < kDepth; ++k) {
-      const int tile = it + k;
-      if (tile < ntiles) {
-        const int pf = tile + kDepth - 1;
-        if (pf < ntiles) load(pf, buf[(k + kDepth - 1) % kDepth]);
-        compute(tile, buf[k]);
+      const int s = it + k;
+      if (s < nsteps) {
+        const int pf = s + kDepth - 1;
+        if (pf < nsteps) load(pf, buf[(k + kDepth - 1) % kDepth]);
+        compute(s, buf[k]);
       }
     }
   }
@@ -228,9 +209,6 @@ const void* pick(bool store_y) {
 }  // namespace
 
 hipError_t launch_quad(int front, bool store_y, const QuadArgs& args, hipStream_t stream) {
-  const int grid = (int)(((int64_t)args.nwork + kWaves - 1) / kWaves);
-  QuadArgs a = args;
-  void* kargs[] = {&a};
   const void* fn = nullptr;
   switch (front) {
     case FRONT_KRON: fn = pick<FRONT_KRON>(store_y); break;
@@ -239,7 +217,11 @@ hipError_t launch_quad(int front, bool store_y, const QuadArgs& args, hipStream_
     case FRONT_HADAMARD: fn = pick<FRONT_HADAMARD>(store_y); break;
     default: return hipErrorInvalidValue;
   }
-  return hipLaunchKernel(fn, dim3(grid), dim3(64 * kWaves), kargs, 0, stream);
+  QuadArgs a = args;
+  a.ngroups = (a.nb + 15) / 16;
+  a.nchunks = chunks_one_round(fn, 64 * kWaves, a.ngroups, (a.T + kWaves - 1) / kWaves);
+  void* kargs[] = {&a};
+  return hipLaunchKernel(fn, dim3(a.ngroups * a.nchunks), dim3(64 * kWaves), kargs, 0, stream);
 }
 
 }  // namespace kq
