@@ -58,7 +58,8 @@
  *
  * Errors.  Argument checks run before any HIP call and write nothing:
  *   KQ_ERR_NULL    a required pointer is NULL while tokens > 0;
- *   KQ_ERR_SHAPE   d <= 0, d % 32 != 0, tokens < 0, tokens * d >= 2^40,
+ *   KQ_ERR_SHAPE   d <= 0, d % 32 != 0, d > 2^24, tokens < 0, tokens >= 2^31,
+ *                  tokens * d >= 2^40,
  *                  nb <= 0, n_split not in 1..3, a stride other than 15 / 0;
  *   KQ_ERR_ALIGN   X, codes, Y, K_bf16, ch_mult not 16-byte aligned, or
  *                  K_params / K_f32 not 4-byte aligned;

@@ -66,7 +66,7 @@ const Overrides& overrides() {
 
 kq_status check_shape(int64_t tokens, int64_t d) {
   if (tokens < 0 || d <= 0 || d % 32 != 0) return KQ_ERR_SHAPE;
-  if (tokens >= (int64_t(1) << 31) || d >= (int64_t(1) << 31) || tokens * d >= (int64_t(1) << 40)) return KQ_ERR_SHAPE;
+  if (tokens >= (int64_t(1) << 31) || d > (int64_t(1) << 24) || tokens * d >= (int64_t(1) << 40)) return KQ_ERR_SHAPE;
   return KQ_OK;
 }
 

@@ -16,9 +16,8 @@ __global__ __launch_bounds__(256) void build_kernel(const float* __restrict__ P,
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)nb * 1024) return;
   const int j = (int)(idx >> 10), r = (int)((idx >> 5) & 31), c = (int)(idx & 31);
-  double G[5][4];
-  factors_f64(P + (int64_t)j * 15, G);
-  const float k = k32_entry(G, r, c);
+  const Factors F = factors_f64(P + (int64_t)j * 15);
+  const float k = k32_entry(F, r, c);
   if (K32) K32[idx] = k;
   if (Kbf) {
     float rest = k;

@@ -37,28 +37,60 @@ __device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w 
 // = [[a, b], [l a, l b + 1/a]] (KroQuant, Sec. 3.2 Eq. (6) as the Pith review
 // quotes it, with the determinant +1 form of U).  l a and l b are exact in
 // fp64; 1/a and the final sum are single correctly rounded operations.
-__device__ __forceinline__ void factor_f64(const float* p, double G[4]) {
+struct Factor {
+  double g00, g01, g10, g11;
+};
+
+// The five factors of a block, G1 first.  Named members, not an array, so
+// that lane-dependent entry selection stays in registers.
+struct Factors {
+  Factor f1, f2, f3, f4, f5;
+};
+
+__device__ __forceinline__ Factor factor_f64(const float* p) {
   const double L = p[0], A = p[1], B = p[2];
   const double inv_a = 1.0 / A;
-  G[0] = A;
-  G[1] = B;
-  G[2] = L * A;
-  G[3] = L * B + inv_a;
+  return Factor{A, B, L * A, L * B + inv_a};
 }
 
-__device__ __forceinline__ void factors_f64(const float* __restrict__ p15, double G[5][4]) {
-#pragma unroll
-  for (int k = 0; k < 5; ++k) factor_f64(p15 + 3 * k, G[k]);
+__device__ __forceinline__ Factors factors_f64(const float* __restrict__ p15) {
+  return Factors{factor_f64(p15), factor_f64(p15 + 3), factor_f64(p15 + 6), factor_f64(p15 + 9),
+                 factor_f64(p15 + 12)};
+}
+
+// Entry [rb][cb] of a factor, rb and cb in {0, 1}.
+__device__ __forceinline__ double pick(Factor g, int rb, int cb) {
+  const double top = cb ? g.g01 : g.g00;
+  const double bottom = cb ? g.g11 : g.g10;
+  return rb ? bottom : top;
 }
 
 // K[r][c] of K = G1 (x) ... (x) G5 (G1 on bit 4 of r and c, G5 on bit 0): the
 // product of one entry per factor, multiplied in factor order in fp64, then
 // rounded once to fp32.
-__device__ __forceinline__ float k32_entry(const double G[5][4], int r, int c) {
-  double p = G[0][2 * ((r >> 4) & 1) + ((c >> 4) & 1)];
-#pragma unroll
-  for (int k = 1; k < 5; ++k) p = p * G[k][2 * ((r >> (4 - k)) & 1) + ((c >> (4 - k)) & 1)];
+__device__ __forceinline__ float k32_entry(Factors F, int r, int c) {
+  double p = pick(F.f1, (r >> 4) & 1, (c >> 4) & 1);
+  p = p * pick(F.f2, (r >> 3) & 1, (c >> 3) & 1);
+  p = p * pick(F.f3, (r >> 2) & 1, (c >> 2) & 1);
+  p = p * pick(F.f4, (r >> 1) & 1, (c >> 1) & 1);
+  p = p * pick(F.f5, r & 1, c & 1);
   return (float)p;
+}
+
+// The factors as 20 doubles (G1 first, each row-major), for staging in LDS.
+__device__ __forceinline__ void store_factor(Factor f, double* out) {
+  out[0] = f.g00;
+  out[1] = f.g01;
+  out[2] = f.g10;
+  out[3] = f.g11;
+}
+
+__device__ __forceinline__ void store_factors(Factors F, double* out) {
+  store_factor(F.f1, out);
+  store_factor(F.f2, out + 4);
+  store_factor(F.f3, out + 8);
+  store_factor(F.f4, out + 12);
+  store_factor(F.f5, out + 16);
 }
 
 // ---------------------------------------------------------------- cross-lane
@@ -98,17 +130,21 @@ __device__ __forceinline__ float local_absmax8(const float y[8]) {
 
 // Exact value of output channel c of one block, as a correctly rounded fp32:
 // the fp64 sum, from +0 in input order r = 0..31, of the exact products
-// x[r] K[r][c] (bf16 times fp32 is exact in fp64), rounded once.  K comes
-// from the 15 scalars.
-struct ExactFromParams {
-  const float* p15;
+// x[r] K[r][c] (bf16 times fp32 is exact in fp64), rounded once, with K the
+// fp32 block (each entry the fp64 product of one entry per factor, rounded).
+// The five factors come in fp64 (20 doubles, G1 first, each row-major),
+// staged in LDS by the kernel's setup.
+struct ExactFromFactors {
+  const double* G;
   __device__ float operator()(const uint16_t* __restrict__ xblk, int c) const {
-    double G[5][4];
-    factors_f64(p15, G);
     double s = 0.0;
+#pragma unroll 1
     for (int r = 0; r < 32; ++r) {
+      double p = G[2 * ((r >> 4) & 1) + ((c >> 4) & 1)];
+#pragma unroll
+      for (int k = 1; k < 5; ++k) p = p * G[4 * k + 2 * ((r >> (4 - k)) & 1) + ((c >> (4 - k)) & 1)];
       const double x = (double)__uint_as_float((unsigned)xblk[r] << 16);
-      s = fma(x, (double)k32_entry(G, r, c), s);
+      s = fma(x, (double)(float)p, s);
     }
     return (float)s;
   }
@@ -120,6 +156,7 @@ struct ExactFromSplit {
   const uint16_t* kblk;  // this block's [3][32][32]
   __device__ float operator()(const uint16_t* __restrict__ xblk, int c) const {
     double s = 0.0;
+#pragma unroll 1
     for (int r = 0; r < 32; ++r) {
       const float hi = __uint_as_float((unsigned)kblk[(0 * 32 + c) * 32 + r] << 16);
       const float mid = __uint_as_float((unsigned)kblk[(1 * 32 + c) * 32 + r] << 16);
@@ -137,6 +174,7 @@ struct ExactFromSplit {
 struct ExactHadamard {
   __device__ float operator()(const uint16_t* __restrict__ xblk, int c) const {
     double s = 0.0;
+#pragma unroll 1
     for (int r = 0; r < 32; ++r) {
       const double x = (double)__uint_as_float((unsigned)xblk[r] << 16);
       s = s + ((__popc(r & c) & 1) ? -x : x);
@@ -208,6 +246,23 @@ __device__ __forceinline__ void mx_epilogue(float y[8], const uint16_t* __restri
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] *= 0x1p-127f;  // restore y for an optional diagnostic store
   }
+}
+
+// ---------------------------------------------------------------- buffers
+
+constexpr uint32_t kOut = 0xFFFFFFF0u;   // buffer offset past every range: load 0 / store dropped
+constexpr int kMaxRecords = 0x7FFFFFFF;  // range cap; in-range offsets stay below 32 d <= 2^29
+constexpr int kRsrcFlags = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family descriptor word 3)
+constexpr int kNT = 2;                   // cache-policy bit of a buffer access: non-temporal (streamed once)
+
+// Raw buffer descriptor over [base, base + bytes): loads at or past `bytes`
+// return zero and stores there are dropped (the hardware range check), so a
+// streaming loop can issue the same memory instructions for full and partial
+// tiles and the compiler can count outstanding loads exactly.  `base` must be
+// wave-uniform (the descriptor lives in scalar registers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes >= kMaxRecords ? kMaxRecords : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRsrcFlags);
 }
 
 // ---------------------------------------------------------------- scheduling

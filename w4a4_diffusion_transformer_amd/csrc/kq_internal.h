@@ -8,8 +8,8 @@ namespace kq {
 
 enum { KSRC_PARAMS = 0, KSRC_SPLIT = 1 };
 
-// Tile decomposition of the MFMA kernels: a workgroup of four waves owns a
-// column group of 8 blocks (512 B of each bf16 row; each wave two blocks,
+// Tile decomposition of the MFMA kernels: a workgroup of eight waves owns a
+// column group of 8 blocks (512 B of each bf16 row; each wave one block,
 // whose K operands stay in its registers) and processes tiles of 16 rows:
 // workgroup (group g, chunk c) takes row tiles c, c + nchunks, ...
 struct MfmaArgs {

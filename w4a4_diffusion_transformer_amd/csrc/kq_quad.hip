@@ -33,20 +33,28 @@ struct Coef {
   float cp[2];    //                          weight of the partner lane's value
 };
 
-__device__ __forceinline__ void setup_coef(Coef& cf, const float* __restrict__ p15, int q) {
-  double G[5][4];
-  factors_f64(p15, G);
-#pragma unroll
-  for (int s = 0; s < 3; ++s)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) cf.g[s][e] = (float)G[4 - s][e];
-  // cross-lane factor k acting on channel bit (4 - k); this lane's bit value is beta
-  const int beta3 = q & 1, beta4 = q >> 1;
-  // y_own = x_own G[beta][beta] + x_partner G[1 - beta][beta]
-  cf.cs[0] = (float)G[1][2 * beta3 + beta3];
-  cf.cp[0] = (float)G[1][2 * (1 - beta3) + beta3];
-  cf.cs[1] = (float)G[0][2 * beta4 + beta4];
-  cf.cp[1] = (float)G[0][2 * (1 - beta4) + beta4];
+__device__ __forceinline__ void set_full(float g[4], const Factor& f) {
+  g[0] = (float)f.g00;
+  g[1] = (float)f.g01;
+  g[2] = (float)f.g10;
+  g[3] = (float)f.g11;
+}
+
+// A cross-lane stage: this lane's channel has bit value beta for the factor:
+// y_own = x_own G[beta][beta] + x_partner G[1 - beta][beta].
+__device__ __forceinline__ void set_cross(float& cs, float& cp, const Factor& f, int beta) {
+  cs = (float)(beta ? f.g11 : f.g00);
+  cp = (float)(beta ? f.g01 : f.g10);
+}
+
+__device__ __forceinline__ void setup_coef(Coef& cf, const float* __restrict__ p15, int q, double* g_out) {
+  const Factors F = factors_f64(p15);
+  if (g_out) store_factors(F, g_out);  // for the exact path
+  set_full(cf.g[0], F.f5);             // channel bit 0
+  set_full(cf.g[1], F.f4);             // bit 1
+  set_full(cf.g[2], F.f3);             // bit 2
+  set_cross(cf.cs[0], cf.cp[0], F.f2, q & 1);   // bit 3: lanes l, l^1
+  set_cross(cf.cs[1], cf.cp[1], F.f1, q >> 1);  // bit 4: lanes l, l^2
 }
 
 // (v[i], v[i | bit]) <- (v[i], v[i | bit]) G for every pair differing in `bit`.
@@ -106,6 +114,7 @@ struct NoExact {
 
 template <int FRONT, bool STORE_Y>
 __global__ __launch_bounds__(64 * kWaves) void quad_kernel(QuadArgs a) {
+  __shared__ double lds_g[FRONT == FRONT_KRON ? 16 : 1][20];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -116,7 +125,10 @@ __global__ __launch_bounds__(64 * kWaves) void quad_kernel(QuadArgs a) {
 
   Coef cf;
   float mult[8];
-  if constexpr (FRONT == FRONT_KRON) setup_coef(cf, a.P + (int64_t)jc * a.pstride, q);
+  if constexpr (FRONT == FRONT_KRON) {
+    setup_coef(cf, a.P + (int64_t)jc * a.pstride, q, wv == 0 && q == 0 ? lds_g[lane >> 2] : nullptr);
+    __syncthreads();
+  }
   if constexpr (FRONT == FRONT_SMOOTH) {
     const f32x4* mp = reinterpret_cast<const f32x4*>(a.m + 32 * jc + 8 * q);
     const f32x4 m0 = mp[0], m1 = mp[1];
@@ -132,19 +144,35 @@ __global__ __launch_bounds__(64 * kWaves) void quad_kernel(QuadArgs a) {
   const int64_t d = a.d;
   const int nrb = (a.T + kWaves - 1) / kWaves;  // row blocks of kWaves rows
   const int nsteps = c < nrb ? (nrb - 1 - c) / a.nchunks + 1 : 0;
-  const uint16_t* xcol = a.X + 32 * jc + 8 * q;
-  auto row_of = [&](int s) { return kWaves * (c + s * a.nchunks) + wv; };
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);  // the wave's row is wave-uniform
+  // this lane's byte offsets within a row (kOut: nothing to move)
+  const uint32_t xoff = live ? (uint32_t)(64 * j + 16 * q) : kOut;
+  const uint32_t coff = live ? (uint32_t)(16 * j + 4 * q) : kOut;
+  const uint32_t soff = live && q == 0 ? (uint32_t)j : kOut;
   u32x4 buf[kDepth];
 
-  auto load = [&](int s, u32x4& b) {
-    const int r = row_of(s);
-    b = (r < a.T && live) ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xcol + (int64_t)r * d))
-                          : u32x4{0, 0, 0, 0};
+  // Wave-uniform cursors advanced by a constant per step (the wave's next
+  // row to load, and the row being computed and stored).  Rows past the end
+  // read zeros and their stores are dropped by the buffer range check, so
+  // every step issues the same memory instructions.
+  const int64_t step_rows = (int64_t)kWaves * a.nchunks;
+  const int xrow_bytes = (int)(2 * d), crow_bytes = (int)(d >> 1), srow_bytes = a.nb;
+  const int64_t row0 = (int64_t)kWaves * c + wvu;
+  int64_t lrow = row0;
+  const uint8_t* lx = reinterpret_cast<const uint8_t*>(a.X) + row0 * xrow_bytes;
+  auto load = [&](int, u32x4& b) {
+    const int n = lrow < a.T ? xrow_bytes : 0;
+    b = __builtin_amdgcn_raw_buffer_load_b128(rsrc(lx, n), xoff, 0, kNT);
+    lrow += step_rows;
+    lx += step_rows * xrow_bytes;
   };
+  int64_t crow = row0;
+  const uint16_t* cx = a.X + row0 * d;
+  uint8_t* cc = a.codes + row0 * crow_bytes;
+  uint8_t* cs = a.scales + row0 * srow_bytes;
 
-  auto compute = [&](int s, const u32x4& b) {
-    const int r = row_of(s);
-    if (r >= a.T) return;  // wave-uniform: one row per wave
+  auto compute = [&](int, const u32x4& b) {
+    const bool in = crow < a.T;
     float y[8];
     unpack8(b, y);
     if constexpr (FRONT == FRONT_KRON) {
@@ -165,36 +193,39 @@ __global__ __launch_bounds__(64 * kWaves) void quad_kernel(QuadArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) y[i] *= kInvSqrt32;
     }
-    const uint16_t* xblk = a.X + (int64_t)r * d + 32 * jc;
+    // rows past the end hold zeros (amax 0): the exact path never runs for them
+    const uint16_t* xblk = (in ? cx : a.X) + 32 * jc;
     unsigned word, byte;
     if constexpr (FRONT == FRONT_KRON) {
-      mx_epilogue<LAYOUT_QUAD, true>(y, xblk, q, ExactFromParams{a.P + (int64_t)jc * a.pstride}, word, byte);
+      mx_epilogue<LAYOUT_QUAD, true>(y, xblk, q, ExactFromFactors{lds_g[lane >> 2]}, word, byte);
     } else if constexpr (FRONT == FRONT_HADAMARD) {
       mx_epilogue<LAYOUT_QUAD, true>(y, xblk, q, ExactHadamard{}, word, byte);
     } else {
       mx_epilogue<LAYOUT_QUAD, false>(y, xblk, q, NoExact{}, word, byte);
     }
-    if (live) {
-      *reinterpret_cast<unsigned*>(a.codes + (int64_t)r * (d >> 1) + 16 * j + 4 * q) = word;
-      if (q == 0) a.scales[(int64_t)r * a.nb + j] = (uint8_t)byte;
-      if constexpr (STORE_Y) {
-        float* yr = a.Y + (int64_t)r * d + 32 * j + 8 * q;
+    __builtin_amdgcn_raw_buffer_store_b32(word, rsrc(cc, in ? crow_bytes : 0), coff, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)byte, rsrc(cs, in ? srow_bytes : 0), soff, 0, 0);
+    if constexpr (STORE_Y) {
+      if (live && in) {
+        float* yr = a.Y + crow * d + 32 * j + 8 * q;
         *reinterpret_cast<f32x4*>(yr) = f32x4{y[0], y[1], y[2], y[3]};
         *reinterpret_cast<f32x4*>(yr + 4) = f32x4{y[4], y[5], y[6], y[7]};
       }
     }
+    crow += step_rows;
+    cx += step_rows * d;
+    cc += step_rows * crow_bytes;
+    cs += step_rows * srow_bytes;
   };
 
 #pragma unroll
-  for (int k = 0; k < kDepth - 1; ++k)
-    if (k < nsteps) load(k, buf[k]);
+  for (int k = 0; k < kDepth - 1; ++k) load(k, buf[k]);
   for (int it = 0; it < nsteps; it += kDepth) {
 #pragma unroll
     for (int k = 0; k < kDepth; ++k) {
       const int s = it + k;
       if (s < nsteps) {
-        const int pf = s + kDepth - 1;
-        if (pf < nsteps) load(pf, buf[(k + kDepth - 1) % kDepth]);
+        load(s + kDepth - 1, buf[(k + kDepth - 1) % kDepth]);
         compute(s, buf[k]);
       }
     }
