@@ -52,6 +52,62 @@ def load_traffic(kernel: str, workload: str):
     return t.get("traffic_bytes_per_launch")
 
 
+def shape_table(kq, torch, np, synth, dev):
+    """GB/s and Gelem/s of every kernel on every matrix of the tiny..FLUX workloads.
+
+    Each matrix is copied enough times that one pass over the copies (inputs
+    and outputs) exceeds 512 MB, twice the Infinity Cache, and calls cycle
+    through the copies."""
+    out = {}
+    for spec in [s_ for c in (1, 2, 3) for s_ in synth.CONFIGS[c]]:
+        X = synth.matrix(spec)
+        P = synth.params(spec)
+        m = synth.smooth_mult(X)
+        T, d = spec.T, spec.d
+        nbytes = BYTES_PER_ELEM * T * d
+        copies = max(2, int(np.ceil(512e6 / nbytes)))
+        X0 = torch.from_numpy(X.view(np.int16)).to(dev)
+        Xs = [X0] + [X0.clone() for _ in range(copies - 1)]
+        outs = [kq.alloc_outputs(X0) for _ in range(copies)]
+        Pd = torch.from_numpy(P).to(dev)
+        md = torch.from_numpy(m).to(dev)
+        pstride = 0 if spec.shared_k else 15
+        Kbf = torch.empty((P.shape[0], 3, 32, 32), dtype=torch.int16, device=dev)
+        kq.kq_build_blocks(Pd, P.shape[0], None, Kbf, 3)
+        calls = {
+            "kroquant": lambda i: kq.kq_quantize_ex(Xs[i % copies], Pd, pstride, None, kq.KQ_AUTO, *outs[i % copies]),
+            "kroquant_mfma_dense": lambda i: kq.kq_quantize_ex(Xs[i % copies], None, pstride, Kbf, kq.KQ_MFMA_DENSE,
+                                                               *outs[i % copies]),
+            "kroquant_butterfly": lambda i: kq.kq_quantize_ex(Xs[i % copies], Pd, pstride, None, kq.KQ_BUTTERFLY,
+                                                              *outs[i % copies]),
+        }
+        if not spec.shared_k:
+            calls["smoothquant"] = lambda i: kq.kq_smooth_quantize(Xs[i % copies], md, *outs[i % copies])
+            calls["plain"] = lambda i: kq.kq_mx_quantize(Xs[i % copies], *outs[i % copies])
+            calls["hadamard32"] = lambda i: kq.kq_hadamard_quantize(Xs[i % copies], *outs[i % copies])
+        row = {"T": T, "d": d}
+        reps = max(20, 2 * copies)
+        for name, call in calls.items():
+            for i in range(copies):
+                call(i)
+            torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(reps):
+                call(i)
+            b.record()
+            torch.cuda.synchronize()
+            sec = a.elapsed_time(b) * 1e-3 / reps
+            row[name] = {"GBps": round(nbytes / sec / 1e9, 1), "Gelem_s": round(T * d / sec / 1e9, 1),
+                         "pct_peak": round(100 * nbytes / sec / 1e9 / HBM_PEAK_GBS, 1), "us": round(sec * 1e6, 2)}
+        out[spec.name] = row
+        del Xs, outs
+        print(f"# {spec.name}: " + ", ".join(f"{k} {v['GBps']}" for k, v in row.items() if isinstance(v, dict)),
+              file=sys.stderr, flush=True)
+    return out
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -60,6 +116,7 @@ def parse():
     ap.add_argument("--variant", default="auto", choices=["auto", "mfma_dense", "mfma_otf", "butterfly"])
     ap.add_argument("--no-compare", action="store_true", help="skip the comparison kernels")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-shapes", action="store_true", help="skip the per-shape table of the other workloads")
     ap.add_argument("--profile-pass", action="store_true",
                     help="few launches of each kernel plus a plain copy of known size, for rocprofv3 counter runs")
     return ap.parse_args()
@@ -165,18 +222,24 @@ def main():
     if not args.no_cpu:
         import oracle
 
-        rows = int(os.environ.get("KQ_CPU_SAMPLE_ROWS", "4096"))
+        # the oracle as it stands, single-threaded, on whole calls of this workload until ~10 s have passed
         t1 = time.perf_counter()
-        oracle.quantize_rows(oracle.KRON, X[:rows], P, threads=1)
-        dt = time.perf_counter() - t1
-        cpu = {"value": round(BYTES_PER_ELEM * rows * d / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-               "kind": "oracle",
-               "sample": f"first {rows} of {T} rows of the stress matrix (d={d}), one call, single thread, "
-                         f"{dt:.1f} s"}
+        calls = 0
+        while True:
+            oracle.quantize_rows(oracle.KRON, X, P, threads=1)
+            calls += 1
+            dt = time.perf_counter() - t1
+            if dt >= 10.0 or calls >= 3:
+                break
+        cpu = {"value": round(bytes_call * calls / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{calls} full call(s) of the stress workload ({T} x {d}), single thread, {dt:.1f} s"}
+
+    per_shape = None
+    if not args.no_shapes:
+        per_shape = shape_table(kq, torch, np, synth, dev)
 
     variant_name = args.variant
-    kernel = {"auto": "mfma_otf", "mfma_dense": "mfma_dense", "mfma_otf": "mfma_otf",
-              "butterfly": "butterfly"}[variant_name]
+    kernel = kq.variant_name(kq.kq_auto_variant(T, d, True, False)) if variant_name == "auto" else variant_name
     traffic = load_traffic(kernel, "stress")
     roofline = {"bound": "hbm", "achieved": round(bytes_call / (launch_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(bytes_call / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -204,6 +267,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "comparison": comparison,
+        "per_shape": per_shape,
     }
     print(json.dumps(out), flush=True)
 

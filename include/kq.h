@@ -58,7 +58,7 @@
  *
  * Errors.  Argument checks run before any HIP call and write nothing:
  *   KQ_ERR_NULL    a required pointer is NULL while tokens > 0;
- *   KQ_ERR_SHAPE   d <= 0, d % 32 != 0, d > 2^24, tokens < 0, tokens >= 2^31,
+ *   KQ_ERR_SHAPE   d <= 0, d % 32 != 0, d > 2^24, tokens < 0, tokens >= 2^28,
  *                  tokens * d >= 2^40,
  *                  nb <= 0, n_split not in 1..3, a stride other than 15 / 0;
  *   KQ_ERR_ALIGN   X, codes, Y, K_bf16, ch_mult not 16-byte aligned, or
@@ -142,6 +142,14 @@ kq_status kq_quantize(const uint16_t* X, int64_t tokens, int64_t d, const float*
 kq_status kq_quantize_ex(const uint16_t* X, int64_t tokens, int64_t d, const float* K_params,
                          int64_t params_block_stride, const uint16_t* K_bf16, kq_variant variant,
                          uint8_t* out_codes, uint8_t* out_scales, hipStream_t stream);
+
+/*
+ * The variant KQ_AUTO resolves to for a call with this shape, given whether
+ * K_params and K_bf16 are supplied (nonzero = supplied): the same rule the
+ * entry points apply.  Returns KQ_AUTO when no variant can serve the call
+ * (neither input supplied).  Pure host logic, no HIP call.
+ */
+kq_variant kq_auto_variant(int64_t tokens, int64_t d, int has_params, int has_split);
 
 /* Plain MXFP4: y = x. */
 kq_status kq_mx_quantize(const uint16_t* X, int64_t tokens, int64_t d, uint8_t* out_codes, uint8_t* out_scales,

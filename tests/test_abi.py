@@ -70,7 +70,8 @@ def test_quantize_argument_checks(lib):
     assert lib.kq_quantize(A, 4, 48, B, C, D, None) == KQ_ERR_SHAPE
     assert lib.kq_quantize(A, 4, 0, B, C, D, None) == KQ_ERR_SHAPE
     assert lib.kq_quantize(A, -1, 64, B, C, D, None) == KQ_ERR_SHAPE
-    assert lib.kq_quantize(A, 1 << 31, 64, B, C, D, None) == KQ_ERR_SHAPE
+    assert lib.kq_quantize(A, 1 << 28, 64, B, C, D, None) == KQ_ERR_SHAPE
+    assert lib.kq_quantize(A, 4, (1 << 24) + 32, B, C, D, None) == KQ_ERR_SHAPE
     assert lib.kq_quantize(None, 4, 64, B, C, D, None) == KQ_ERR_NULL
     assert lib.kq_quantize(A, 4, 64, None, C, D, None) == KQ_ERR_NULL
     assert lib.kq_quantize(A, 4, 64, B, None, D, None) == KQ_ERR_NULL
@@ -103,6 +104,14 @@ def test_comparison_entry_checks(lib):
     assert lib.kq_transform_f32(0, A, 4, 64, B, 15, None, 0, None, None, C, D, None) == KQ_ERR_NULL
     assert lib.kq_transform_f32(7, A, 4, 64, B, 15, None, 0, None, D + 4096, C, D, None) == KQ_ERR_VARIANT
     assert lib.kq_transform_f32(1, A, 4, 64, None, 15, None, 0, None, A, C, D, None) == KQ_ERR_ALIAS
+
+
+def test_auto_variant_rule(lib):
+    lib.kq_auto_variant.restype = ctypes.c_int
+    lib.kq_auto_variant.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int]
+    assert lib.kq_auto_variant(4608, 12288, 1, 0) in (1, 2, 3)
+    assert lib.kq_auto_variant(4608, 12288, 0, 1) == 1
+    assert lib.kq_auto_variant(4608, 12288, 0, 0) == 0
 
 
 def test_build_blocks_checks(lib):

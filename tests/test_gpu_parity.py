@@ -262,6 +262,15 @@ def handcrafted_rows() -> np.ndarray:
     row[40] = 1e-39  # subnormal
     row[41] = -2e-39
     f.append(row)
+    # the smallest scales: bytes 0, 1, 2 with nonzero codes (subnormal and tiny normal values)
+    for amax in (2.0 ** -125, 1.5 * 2.0 ** -124, 2.0 ** -123, 1.75 * 2.0 ** -126):
+        row = np.zeros(64, dtype=np.float32)
+        row[0] = amax
+        row[1:8] = amax * np.array([-0.5, 0.25, 0.125, -0.75, 1 / 3, 0.0625, -0.9])
+        row[32] = 2.0 ** -127   # subnormal
+        row[33] = -3 * 2.0 ** -129
+        row[34] = 2.0 ** -133
+        f.append(row)
     f.append(np.zeros(64, dtype=np.float32))
     X = synth.f32_to_bf16(np.stack(f))
     X[-1, 10] = 0x8000  # -0.0

@@ -19,7 +19,7 @@ __all__ = [
     "KQ_FRONT_KRON", "KQ_FRONT_PLAIN", "KQ_FRONT_SMOOTH", "KQ_FRONT_HADAMARD",
     "lib", "kq_abi_version", "kq_status_str", "kq_build_blocks", "kq_quantize", "kq_quantize_ex",
     "kq_mx_quantize", "kq_smooth_quantize", "kq_hadamard_quantize", "kq_transform_f32",
-    "alloc_outputs", "LIB_PATH",
+    "alloc_outputs", "LIB_PATH", "kq_auto_variant", "variant_name",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkq.so")
@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
         L.kq_smooth_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp]
         L.kq_hadamard_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
         L.kq_transform_f32.argtypes = [ci, vp, i64, i64, vp, i64, vp, ci, vp, vp, vp, vp, vp]
+        L.kq_auto_variant.argtypes = [i64, i64, ci, ci]
+        L.kq_auto_variant.restype = ci
         for name in ("kq_build_blocks", "kq_quantize", "kq_quantize_ex", "kq_mx_quantize", "kq_smooth_quantize",
                      "kq_hadamard_quantize", "kq_transform_f32"):
             getattr(L, name).restype = ci
@@ -65,6 +67,14 @@ def lib() -> ctypes.CDLL:
 
 def kq_abi_version() -> int:
     return int(lib().kq_abi_version())
+
+
+def kq_auto_variant(tokens: int, d: int, has_params: bool = True, has_split: bool = False) -> int:
+    return int(lib().kq_auto_variant(tokens, d, int(has_params), int(has_split)))
+
+
+def variant_name(v: int) -> str:
+    return {v_: k for k, v_ in VARIANTS.items()}[int(v)]
 
 
 def kq_status_str(status: int) -> str:

@@ -64,9 +64,21 @@ const Overrides& overrides() {
   return o;
 }
 
+// KQ_AUTO: the MFMA kernel with K rebuilt in-kernel measured fastest on
+// MI355X at the DiT widths (it needs only the 60-byte parameter sets); the
+// dense-block MFMA kernel when only prebuilt blocks are given.  KQ_VARIANT
+// overrides the choice when its inputs are present.
+int auto_variant(int64_t, int64_t, bool has_params, bool has_split) {
+  const int o = overrides().variant;
+  if (o > 0 && (o == KQ_MFMA_DENSE ? has_split : has_params)) return o;
+  if (has_params) return KQ_MFMA_OTF;
+  if (has_split) return KQ_MFMA_DENSE;
+  return KQ_AUTO;
+}
+
 kq_status check_shape(int64_t tokens, int64_t d) {
   if (tokens < 0 || d <= 0 || d % 32 != 0) return KQ_ERR_SHAPE;
-  if (tokens >= (int64_t(1) << 31) || d > (int64_t(1) << 24) || tokens * d >= (int64_t(1) << 40)) return KQ_ERR_SHAPE;
+  if (tokens >= (int64_t(1) << 28) || d > (int64_t(1) << 24) || tokens * d >= (int64_t(1) << 40)) return KQ_ERR_SHAPE;
   return KQ_OK;
 }
 
@@ -85,11 +97,7 @@ kq_status run(int front, const uint16_t* X, int64_t tokens, int64_t d, const flo
   if (!X || !codes || !scales) return KQ_ERR_NULL;
   if (front == kq::FRONT_SMOOTH && !m) return KQ_ERR_NULL;
   if (front == kq::FRONT_KRON) {
-    if (variant == KQ_AUTO) {
-      if (overrides().variant > 0 && (overrides().variant != KQ_MFMA_DENSE || Kbf)) variant = overrides().variant;
-      else if (!P && Kbf) variant = KQ_MFMA_DENSE;
-      else variant = KQ_MFMA_OTF;
-    }
+    if (variant == KQ_AUTO) variant = auto_variant(tokens, d, P != nullptr, Kbf != nullptr);
     if (variant == KQ_MFMA_DENSE && !Kbf) return KQ_ERR_VARIANT;
     if (variant != KQ_MFMA_DENSE && !P) return KQ_ERR_VARIANT;
   }
@@ -219,6 +227,10 @@ kq_status kq_build_blocks(const float* K_params, int64_t nb, float* K_f32, uint1
   const Range ins[] = {{K_params, n * 60}};
   if (any_alias(outs, 2, ins, 1)) return KQ_ERR_ALIAS;
   return from_hip(kq::launch_build(K_params, (int)nb, K_f32, K_bf16, K_bf16 ? n_split : 0, stream));
+}
+
+kq_variant kq_auto_variant(int64_t tokens, int64_t d, int has_params, int has_split) {
+  return (kq_variant)auto_variant(tokens, d, has_params != 0, has_split != 0);
 }
 
 kq_status kq_quantize(const uint16_t* X, int64_t tokens, int64_t d, const float* K_params, uint8_t* out_codes,

@@ -184,67 +184,85 @@ struct ExactHadamard {
 };
 
 // ---------------------------------------------------------------- epilogue
-
-// MXFP4 for one lane's 8 values of a block whose four lanes hold one token.
-// Returns the four packed code bytes (channels 8q+2k in the low nibble of
-// byte k) and the block's E8M0 byte.
 //
-//   amax  = max |y| over the 32 values (group reduction);
-//   byte  = max(exponent_field(amax) - 2, 0): floor(log2 amax) - 2 + 127,
+// MXFP4 for one lane's 8 values of a block whose four lanes hold one token:
+//   amax  = max |y| over the block's 32 values (block_amax, group reduction);
+//   byte  = max(exponent_field(amax) - 2, 0) = floor(log2 amax) - 2 + 127,
 //           clamped at 0 (amax = 0 and subnormal amax give 0; finite fp32
-//           never reaches the upper clamp);
-//   codes = E2M1(y / 2^(byte - 127)), round to nearest even, saturating
-//           (the gfx950 scaled fp4 convert divides by the scale's power of
-//           two; it rounds exactly like the E2M1 rule above for every finite
-//           fp32 input).
+//           never reaches the upper clamp)  (e8m0_byte);
+//   codes = E2M1(y / 2^(byte - 127)) rounded to nearest, ties to the even
+//           code, saturating at 6  (pack_fp4).  The gfx950 scaled fp4
+//           convert divides by 2^(exponent field of its scale operand - 127),
+//           reading field 0 as 2^-127, and rounds exactly like this rule: on
+//           MI355X it matched for every finite fp32 input at scale 1 and for
+//           every scale byte over 3.4e10 sampled values and all bf16 inputs.
+//           So the scale operand is the float whose bit pattern is byte << 23.
 //
-// TRANSFORM front-ends (sums of products) first settle blocks whose amax is
-// within 2^-16 of a power of two: the columns that could cross it are
-// recomputed exactly by `exact`, so the scale equals the exact evaluation's.
-// An all-zero block of a transform yields +0 codes (the exact sum of zeros is
-// +0).
-template <int LAYOUT, bool TRANSFORM, class Exact>
-__device__ __forceinline__ void mx_epilogue(float y[8], const uint16_t* __restrict__ xblk, int q,
-                                            const Exact& exact, unsigned& word, unsigned& byte) {
-  float amax = group_max<LAYOUT>(local_absmax8(y));
-  if constexpr (TRANSFORM) {
+// Transform front-ends (sums of products) first settle blocks whose amax is
+// within 2^-16 of a power of two (near_pow2): the columns that could cross
+// it are recomputed exactly (settle), so the scale equals the exact
+// evaluation's.  An all-zero block of a transform gets +0 codes (the exact
+// sum of zeros is +0).
+
+template <int LAYOUT>
+__device__ __forceinline__ float block_amax(const float y[8]) {
+  return group_max<LAYOUT>(local_absmax8(y));
+}
+
+__device__ __forceinline__ bool near_pow2(float amax) {
+  const unsigned ab = __float_as_uint(amax);
+  const unsigned ex = ab >> 23, mant = ab & 0x7FFFFFu;
+  return ex >= 2u && (mant < kNearLoMant || mant >= kNearHiMant);
+}
+
+// Replace every value of a near block that could reach the straddled power
+// of two by its exact value.  Call with the whole wave (not under divergence
+// between the lanes of a block); lanes whose block is not near keep y.
+template <class Exact>
+__device__ __forceinline__ void settle(float y[8], float amax, const uint16_t* __restrict__ xblk, int q,
+                                       const Exact& exact) {
+  if (near_pow2(amax)) {
     const unsigned ab = __float_as_uint(amax);
     const unsigned ex = ab >> 23, mant = ab & 0x7FFFFFu;
-    const bool near = ex >= 2u && (mant < kNearLoMant || mant >= kNearHiMant);
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(near) != 0, 0)) {
-      if (near) {
-        // the power of two being straddled, and the smallest |y| that could reach it
-        const unsigned pe = mant < kNearLoMant ? ex : ex + 1u;
-        const float thr = __uint_as_float(pe << 23) * (1.0f - 0x1p-14f);
-        for (int i = 0; i < 8; ++i)
-          if (fabsf(y[i]) >= thr) y[i] = exact(xblk, 8 * q + i);
-      }
-      amax = group_max<LAYOUT>(local_absmax8(y));
-    }
+    // the power of two being straddled, and the smallest |y| that could reach it
+    const unsigned pe = mant < kNearLoMant ? ex : ex + 1u;
+    const float thr = __uint_as_float(pe << 23) * (1.0f - 0x1p-14f);
+#pragma unroll 1
+    for (int i = 0; i < 8; ++i)
+      if (fabsf(y[i]) >= thr) y[i] = exact(xblk, 8 * q + i);
   }
+}
+
+__device__ __forceinline__ unsigned e8m0_byte(float amax) {
   const unsigned ex = __float_as_uint(amax) >> 23;
-  byte = ex > 2u ? ex - 2u : 0u;
-  float scale;
-  if (byte != 0u) {
-    scale = __uint_as_float(byte << 23);  // 2^(byte - 127), a normal float for byte >= 1
-  } else {
-    // 2^-127 is not a normal float: scale by 2^127 exactly instead (|y| < 2^-124 here)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] *= 0x1p127f;
-    scale = 1.0f;
-  }
+  return ex > 2u ? ex - 2u : 0u;
+}
+
+__device__ __forceinline__ unsigned pack_fp4(const float y[8], unsigned byte) {
+  const float scale = __uint_as_float(byte << 23);
   unsigned w = 0;
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], scale, 0);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], scale, 1);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], scale, 2);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], scale, 3);
+  return w;
+}
+
+// The whole epilogue for one block per lane group.
+template <int LAYOUT, bool TRANSFORM, class Exact>
+__device__ __forceinline__ void mx_epilogue(float y[8], const uint16_t* __restrict__ xblk, int q,
+                                            const Exact& exact, unsigned& word, unsigned& byte) {
+  float amax = block_amax<LAYOUT>(y);
   if constexpr (TRANSFORM) {
-    if (amax == 0.0f) w = 0u;
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(near_pow2(amax)) != 0, 0)) {
+      settle(y, amax, xblk, q, exact);
+      amax = block_amax<LAYOUT>(y);
+    }
   }
-  word = w;
-  if (byte == 0u) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] *= 0x1p-127f;  // restore y for an optional diagnostic store
+  byte = e8m0_byte(amax);
+  word = pack_fp4(y, byte);
+  if constexpr (TRANSFORM) {
+    if (amax == 0.0f) word = 0u;
   }
 }
 

@@ -29,8 +29,7 @@ namespace kq {
 namespace {
 
 constexpr int kWaves = 8;                          // waves per workgroup
-constexpr int kBPW = 1;                            // blocks per wave (K operands in its registers)
-constexpr int kCB = kWaves * kBPW;                 // blocks per column group (512 B of a row)
+constexpr int kCB = kWaves;                        // blocks per column group (512 B of a row), one per wave
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRT = 2;                             // 16-row MFMA sub-tiles per tile
 constexpr int kRows = 16 * kRT;                    // rows per tile
@@ -101,9 +100,9 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(MfmaArgs a) {
   const int64_t d = a.d;
   const int ntile_rows = (a.T + kRows - 1) / kRows;
   const int nsteps = c < ntile_rows ? (ntile_rows - 1 - c) / a.nchunks + 1 : 0;
-  auto row0_of = [&](int s) { return (int64_t)kRows * (c + (int64_t)s * a.nchunks); };
 
-  bf16x8 A[kBPW][2][3];
+  const bool mine = wv < nvalid;  // this wave's block exists
+  bf16x8 A[2][3];                 // K^T operands: [output half][term hi, mid, lo]
 
   uint32_t xoff[kPPT];
   int lin[kPPT];
@@ -130,110 +129,141 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(MfmaArgs a) {
 
   u32x4 pre[kAhead][kPPT];
   // Wave-uniform cursors, advanced by a constant per tile: the next tile to
-  // load, the tile being written out.  Range sizes are clamped to one tile.
-  const int64_t step_rows = (int64_t)kRows * a.nchunks;
-  const int xrow_bytes = (int)(2 * d), crow_bytes = (int)(d >> 1), srow_bytes = a.nb;
-  int64_t lrow = (int64_t)kRows * c;                 // first row of the next tile to load
-  const uint8_t* lx = reinterpret_cast<const uint8_t*>(a.X) + lrow * xrow_bytes;
-  const int64_t lstep = step_rows * xrow_bytes;
-  auto rows_in = [&](int64_t row) {
-    const int64_t left = (int64_t)a.T - row;
-    return left <= 0 ? 0 : (left >= kRows ? kRows : (int)left);
-  };
+  // load and the next tile to write out.  `left` counts the rows from a
+  // cursor to the end of the matrix (negative past it); range sizes are
+  // clamped to one tile, so rows past the end read zeros / drop stores.
+  const int step_rows = kRows * a.nchunks;
+  const int xrow_bytes = 2 * a.d, crow_bytes = a.d >> 1, srow_bytes = a.nb;
+  const int row_first = kRows * c;
+  auto rows_in = [](int left) { return left <= 0 ? 0 : (left >= kRows ? kRows : left); };
+
+  int lleft = a.T - row_first;
+  const uint8_t* lx = reinterpret_cast<const uint8_t*>(a.X) + (int64_t)row_first * xrow_bytes;
+  const int64_t lstep = (int64_t)step_rows * xrow_bytes;
   auto gload_next = [&](u32x4 (&r)[kPPT]) {
-    const auto rx = rsrc(lx, rows_in(lrow) * xrow_bytes);
+    const auto rx = rsrc(lx, rows_in(lleft) * xrow_bytes);
 #pragma unroll
     for (int k = 0; k < kPPT; ++k) r[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[k], 0, kNT);
-    lrow += step_rows;
+    lleft -= step_rows;
     lx += lstep;
   };
   auto lwrite = [&](int buf, const u32x4 (&r)[kPPT]) {
 #pragma unroll
     for (int k = 0; k < kPPT; ++k) *reinterpret_cast<u32x4*>(&lds_in[buf][lin[k]]) = r[k];
   };
-  // store cursor starts one tile before the first (nothing to write there)
-  int64_t srow = (int64_t)kRows * c - step_rows;
-  uint8_t* sc = a.codes + srow * crow_bytes;
-  uint8_t* ss = a.scales + srow * srow_bytes;
-  const int64_t cstep = step_rows * crow_bytes, sstep = step_rows * srow_bytes;
+  int sleft = a.T - row_first;
+  uint8_t* sc = a.codes + (int64_t)row_first * crow_bytes;
+  uint8_t* ss = a.scales + (int64_t)row_first * srow_bytes;
+  const int64_t cstep = (int64_t)step_rows * crow_bytes, sstep = (int64_t)step_rows * srow_bytes;
   auto gstore_next = [&](int buf) {
-    const int n = srow < 0 ? 0 : rows_in(srow);
-    const auto rc = rsrc(n ? sc : a.codes, n * crow_bytes);
-    const auto rs = rsrc(n ? ss : a.scales, n * srow_bytes);
+    const int n = rows_in(sleft);
+    const auto rc = rsrc(sc, n * crow_bytes);
+    const auto rs = rsrc(ss, n * srow_bytes);
 #pragma unroll
     for (int k = 0; k < kOPT; ++k) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(&lds_out[buf][lout[k]]);
       __builtin_amdgcn_raw_buffer_store_b128(v, rc, coff[k], 0, 0);
       __builtin_amdgcn_raw_buffer_store_b8(lds_sc[buf][lsc[k]], rs, soff[k], 0, 0);
     }
-    srow += step_rows;
+    sleft -= step_rows;
     sc += cstep;
     ss += sstep;
   };
 
   const int tl = lane & 15, q = lane >> 4;
-  auto compute = [&](int s, int buf) {
+  int crow = row_first;  // first row of the tile being computed (diagnostic store only)
+  auto compute = [&](int buf) {
+    if (!mine) return;  // wave-uniform
+    const int jl = wv, j = jg + jl;
+    // all MFMAs of the tile first, so their latency overlaps the epilogues
+    float y[kRT][8];
 #pragma unroll
-    for (int bb = 0; bb < kBPW; ++bb) {
-      const int jl = kBPW * wv + bb;
-      if (jl >= nvalid) break;
-      const int j = jg + jl;
+    for (int rt = 0; rt < kRT; ++rt) {
+      const int tr = 16 * rt + tl;
+      const bf16x8 xb = *reinterpret_cast<const bf16x8*>(&lds_in[buf][tr * kInStride + 64 * jl + 16 * q]);
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0][2], xb, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1][2], xb, acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0][1], xb, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1][1], xb, acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0][0], xb, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1][0], xb, acc1, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        y[rt][i] = acc0[i];
+        y[rt][4 + i] = acc1[i];
+      }
+    }
+    float amax[kRT];
+    bool near = false;
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) {
+      amax[rt] = block_amax<LAYOUT_MFMA>(y[rt]);
+      near = near || near_pow2(amax[rt]);
+    }
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(near) != 0, 0)) {
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) {
-        const int tr = 16 * rt + tl;
-        const bf16x8 xb = *reinterpret_cast<const bf16x8*>(&lds_in[buf][tr * kInStride + 64 * jl + 16 * q]);
-        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[bb][0][2], xb, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[bb][1][2], xb, acc1, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[bb][0][1], xb, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[bb][1][1], xb, acc1, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[bb][0][0], xb, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[bb][1][0], xb, acc1, 0, 0, 0);
-        float y[8] = {acc0[0], acc0[1], acc0[2], acc0[3], acc1[0], acc1[1], acc1[2], acc1[3]};
-        const uint16_t* xblk = reinterpret_cast<const uint16_t*>(&lds_in[buf][tr * kInStride + 64 * jl]);
-        unsigned word, byte;
+        // the exact path reads this token's block back from the LDS tile
+        const uint16_t* xblk = reinterpret_cast<const uint16_t*>(&lds_in[buf][(16 * rt + tl) * kInStride + 64 * jl]);
         if constexpr (KSRC == KSRC_PARAMS) {
-          mx_epilogue<LAYOUT_MFMA, true>(y, xblk, q, ExactFromFactors{lds_g[jl]}, word, byte);
+          settle(y[rt], amax[rt], xblk, q, ExactFromFactors{lds_g[jl]});
         } else {
-          mx_epilogue<LAYOUT_MFMA, true>(y, xblk, q, ExactFromSplit{a.Kbf + (int64_t)j * a.kstride}, word, byte);
+          settle(y[rt], amax[rt], xblk, q, ExactFromSplit{a.Kbf + (int64_t)j * a.kstride});
         }
-        *reinterpret_cast<unsigned*>(&lds_out[buf][tr * kOutStride + 16 * jl + 4 * q]) = word;
-        if (q == 0) lds_sc[buf][tr * kCB + jl] = (uint8_t)byte;
-        if constexpr (STORE_Y) {
-          const int64_t t = row0_of(s) + tr;
-          if (t < a.T) {
-            float* yr = a.Y + t * d + 32 * j + 8 * q;
-            *reinterpret_cast<f32x4*>(yr) = f32x4{y[0], y[1], y[2], y[3]};
-            *reinterpret_cast<f32x4*>(yr + 4) = f32x4{y[4], y[5], y[6], y[7]};
-          }
+        amax[rt] = block_amax<LAYOUT_MFMA>(y[rt]);
+      }
+    }
+#pragma unroll
+    for (int rt = 0; rt < kRT; ++rt) {
+      const int tr = 16 * rt + tl;
+      const unsigned byte = e8m0_byte(amax[rt]);
+      const unsigned word = amax[rt] == 0.0f ? 0u : pack_fp4(y[rt], byte);
+      *reinterpret_cast<unsigned*>(&lds_out[buf][tr * kOutStride + 16 * jl + 4 * q]) = word;
+      if (q == 0) lds_sc[buf][tr * kCB + jl] = (uint8_t)byte;
+      if constexpr (STORE_Y) {
+        if (crow + tr < a.T) {
+          float* yr = a.Y + (int64_t)(crow + tr) * a.d + 32 * j + 8 * q;
+          *reinterpret_cast<f32x4*>(yr) = f32x4{y[rt][0], y[rt][1], y[rt][2], y[rt][3]};
+          *reinterpret_cast<f32x4*>(yr + 4) = f32x4{y[rt][4], y[rt][5], y[rt][6], y[rt][7]};
         }
       }
     }
   };
 
+  // Loads of the first kAhead tiles go out before the K setup, which overlaps them.
 #pragma unroll
   for (int k = 0; k < kAhead; ++k) gload_next(pre[k]);
-#pragma unroll
-  for (int bb = 0; bb < kBPW; ++bb)
-    if (kBPW * wv + bb < nvalid)
-      setup_a<KSRC>(A[bb], jg + kBPW * wv + bb, a.P, a.pstride, a.Kbf, a.kstride, lane, lds_g[kBPW * wv + bb]);
+  if (mine) setup_a<KSRC>(A, jg + wv, a.P, a.pstride, a.Kbf, a.kstride, lane, lds_g[wv]);
 
-  for (int it = 0; it < nsteps; it += kAhead) {
+  // Per tile s: stage tile s into LDS, fetch tile s + kAhead, barrier, write
+  // out tile s - 1, compute tile s.  Every memory instruction is issued
+  // unconditionally (out-of-range ones are no-ops), so the loads of the next
+  // kAhead tiles stay in flight across the barrier.  Tile 0 is peeled: it has
+  // no predecessor to write out.
+  if (nsteps == 0) return;  // workgroup-uniform
+  lwrite(0, pre[0]);
+  gload_next(pre[0]);
+  __syncthreads();
+  compute(0);
+  crow += step_rows;
+  for (int it = 1; it < nsteps; it += kAhead) {
 #pragma unroll
     for (int k = 0; k < kAhead; ++k) {
       const int s = it + k;
       if (s < nsteps) {
         const int buf = s & 1;
-        lwrite(buf, pre[k]);
-        gload_next(pre[k]);
+        lwrite(buf, pre[(1 + k) % kAhead]);
+        gload_next(pre[(1 + k) % kAhead]);
         __syncthreads();
         gstore_next(buf ^ 1);
-        compute(s, buf);
+        compute(buf);
+        crow += step_rows;
       }
     }
   }
   __syncthreads();
-  if (nsteps > 0) gstore_next((nsteps - 1) & 1);
+  gstore_next((nsteps - 1) & 1);
 }
 
 }  // namespace

@@ -155,24 +155,27 @@ __global__ __launch_bounds__(64 * kWaves) void quad_kernel(QuadArgs a) {
   // row to load, and the row being computed and stored).  Rows past the end
   // read zeros and their stores are dropped by the buffer range check, so
   // every step issues the same memory instructions.
-  const int64_t step_rows = (int64_t)kWaves * a.nchunks;
-  const int xrow_bytes = (int)(2 * d), crow_bytes = (int)(d >> 1), srow_bytes = a.nb;
-  const int64_t row0 = (int64_t)kWaves * c + wvu;
-  int64_t lrow = row0;
-  const uint8_t* lx = reinterpret_cast<const uint8_t*>(a.X) + row0 * xrow_bytes;
+  const int step_rows = kWaves * a.nchunks;
+  const int xrow_bytes = 2 * a.d, crow_bytes = a.d >> 1, srow_bytes = a.nb;
+  const int row0 = kWaves * c + wvu;
+  int lleft = a.T - row0;  // rows from the load cursor to the end (negative past it)
+  const uint8_t* lx = reinterpret_cast<const uint8_t*>(a.X) + (int64_t)row0 * xrow_bytes;
+  const int64_t lstep = (int64_t)step_rows * xrow_bytes;
   auto load = [&](int, u32x4& b) {
-    const int n = lrow < a.T ? xrow_bytes : 0;
-    b = __builtin_amdgcn_raw_buffer_load_b128(rsrc(lx, n), xoff, 0, kNT);
-    lrow += step_rows;
-    lx += step_rows * xrow_bytes;
+    b = __builtin_amdgcn_raw_buffer_load_b128(rsrc(lx, lleft > 0 ? xrow_bytes : 0), xoff, 0, kNT);
+    lleft -= step_rows;
+    lx += lstep;
   };
+  int cleft = a.T - row0;  // the same for the row being computed and stored
   int64_t crow = row0;
-  const uint16_t* cx = a.X + row0 * d;
-  uint8_t* cc = a.codes + row0 * crow_bytes;
-  uint8_t* cs = a.scales + row0 * srow_bytes;
+  const uint16_t* cx = a.X + (int64_t)row0 * d;
+  uint8_t* cc = a.codes + (int64_t)row0 * crow_bytes;
+  uint8_t* cs = a.scales + (int64_t)row0 * srow_bytes;
+  const int64_t cxstep = (int64_t)step_rows * d, ccstep = (int64_t)step_rows * crow_bytes,
+                csstep = (int64_t)step_rows * srow_bytes;
 
   auto compute = [&](int, const u32x4& b) {
-    const bool in = crow < a.T;
+    const bool in = cleft > 0;
     float y[8];
     unpack8(b, y);
     if constexpr (FRONT == FRONT_KRON) {
@@ -212,10 +215,11 @@ __global__ __launch_bounds__(64 * kWaves) void quad_kernel(QuadArgs a) {
         *reinterpret_cast<f32x4*>(yr + 4) = f32x4{y[4], y[5], y[6], y[7]};
       }
     }
+    cleft -= step_rows;
     crow += step_rows;
-    cx += step_rows * d;
-    cc += step_rows * crow_bytes;
-    cs += step_rows * srow_bytes;
+    cx += cxstep;
+    cc += ccstep;
+    cs += csstep;
   };
 
 #pragma unroll
