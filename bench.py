@@ -53,11 +53,11 @@ def load_traffic(kernel: str, workload: str):
 
 
 def shape_table(kq, torch, np, synth, dev):
-    """GB/s and Gelem/s of every kernel on every matrix of the tiny..FLUX workloads.
+    """GB/s and Gelem/s of every kernel on every matrix of the PixArt, SANA and FLUX workloads.
 
     Each matrix is copied enough times that one pass over the copies (inputs
     and outputs) exceeds 512 MB, twice the Infinity Cache, and calls cycle
-    through the copies."""
+    through the copies back to back on one stream."""
     out = {}
     for spec in [s_ for c in (1, 2, 3) for s_ in synth.CONFIGS[c]]:
         X = synth.matrix(spec)
@@ -74,28 +74,37 @@ def shape_table(kq, torch, np, synth, dev):
         pstride = 0 if spec.shared_k else 15
         Kbf = torch.empty((P.shape[0], 3, 32, 32), dtype=torch.int16, device=dev)
         kq.kq_build_blocks(Pd, P.shape[0], None, Kbf, 3)
+        # Calls go straight to the C ABI with pointers marshalled once: these kernels run
+        # 10-40 us, so per-call host overhead must stay well below that for back-to-back
+        # launches on the stream (HIP graph replay was measured to add ~9 us per kernel).
+        L = kq.lib()
+        stream = torch.cuda.current_stream().cuda_stream
+        xs = [x.data_ptr() for x in Xs]
+        os_ = [(c_.data_ptr(), s_.data_ptr()) for c_, s_ in outs]
+        pp, mp, kp = Pd.data_ptr(), md.data_ptr(), Kbf.data_ptr()
         calls = {
-            "kroquant": lambda i: kq.kq_quantize_ex(Xs[i % copies], Pd, pstride, None, kq.KQ_AUTO, *outs[i % copies]),
-            "kroquant_mfma_dense": lambda i: kq.kq_quantize_ex(Xs[i % copies], None, pstride, Kbf, kq.KQ_MFMA_DENSE,
-                                                               *outs[i % copies]),
-            "kroquant_butterfly": lambda i: kq.kq_quantize_ex(Xs[i % copies], Pd, pstride, None, kq.KQ_BUTTERFLY,
-                                                              *outs[i % copies]),
+            "kroquant": (L.kq_quantize_ex, lambda i: (xs[i], T, d, pp, pstride, None, kq.KQ_AUTO, *os_[i], stream)),
+            "kroquant_mfma_dense": (L.kq_quantize_ex,
+                                    lambda i: (xs[i], T, d, None, pstride, kp, kq.KQ_MFMA_DENSE, *os_[i], stream)),
+            "kroquant_butterfly": (L.kq_quantize_ex,
+                                   lambda i: (xs[i], T, d, pp, pstride, None, kq.KQ_BUTTERFLY, *os_[i], stream)),
         }
         if not spec.shared_k:
-            calls["smoothquant"] = lambda i: kq.kq_smooth_quantize(Xs[i % copies], md, *outs[i % copies])
-            calls["plain"] = lambda i: kq.kq_mx_quantize(Xs[i % copies], *outs[i % copies])
-            calls["hadamard32"] = lambda i: kq.kq_hadamard_quantize(Xs[i % copies], *outs[i % copies])
+            calls["smoothquant"] = (L.kq_smooth_quantize, lambda i: (xs[i], T, d, mp, *os_[i], stream))
+            calls["plain"] = (L.kq_mx_quantize, lambda i: (xs[i], T, d, *os_[i], stream))
+            calls["hadamard32"] = (L.kq_hadamard_quantize, lambda i: (xs[i], T, d, *os_[i], stream))
         row = {"T": T, "d": d}
-        reps = max(20, 2 * copies)
-        for name, call in calls.items():
-            for i in range(copies):
-                call(i)
+        for name, (fn, mk) in calls.items():
+            argv = [mk(i) for i in range(copies)]
+            for a_ in argv:  # warm-up
+                assert fn(*a_) == 0
             torch.cuda.synchronize()
+            reps = max(60, 4 * copies)
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record()
             for i in range(reps):
-                call(i)
+                fn(*argv[i % copies])
             b.record()
             torch.cuda.synchronize()
             sec = a.elapsed_time(b) * 1e-3 / reps
