@@ -96,10 +96,14 @@ def shape_table(kq, torch, np, synth, dev):
         row = {"T": T, "d": d}
         for name, (fn, mk) in calls.items():
             argv = [mk(i) for i in range(copies)]
-            for a_ in argv:  # warm-up
-                assert fn(*a_) == 0
-            torch.cuda.synchronize()
             reps = max(60, 4 * copies)
+            # warm-up of at least 100 ms of back-to-back calls: clocks drop while the GPU
+            # idles (input generation runs on the host), and they take a while to come back
+            t_warm = time.perf_counter() + 0.1
+            while time.perf_counter() < t_warm:
+                for i in range(reps):
+                    assert fn(*argv[i % copies]) == 0
+                torch.cuda.synchronize()
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record()
@@ -120,8 +124,8 @@ def shape_table(kq, torch, np, synth, dev):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--variant", default="auto", choices=["auto", "mfma_dense", "mfma_otf", "butterfly"])
     ap.add_argument("--no-compare", action="store_true", help="skip the comparison kernels")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")

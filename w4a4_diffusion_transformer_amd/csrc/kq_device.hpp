@@ -283,6 +283,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRsrcFlags);
 }
 
+// Same, with every descriptor field moved to scalar registers.  Where the
+// compiler evaluates a cursor's clamp in vector registers it cannot prove the
+// descriptor uniform and wraps each buffer access in a loop over the
+// distinct descriptors of the wave; reading the fields through readfirstlane
+// (they are uniform by construction) removes those loops.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_uniform(const void* base, int64_t bytes) {
+  const int n = __builtin_amdgcn_readfirstlane(bytes <= 0 ? 0 : (bytes >= kMaxRecords ? kMaxRecords : (int)bytes));
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint64_t hi = (uint64_t)(unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(b >> 32));
+  const uint64_t lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)b);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((hi << 32) | lo), (short)0, n, kRsrcFlags);
+}
+
 // ---------------------------------------------------------------- scheduling
 
 // Workgroups are handed to the 8 XCDs round-robin.  Renumber them so that

@@ -10,8 +10,12 @@ enum { KSRC_PARAMS = 0, KSRC_SPLIT = 1 };
 
 // Tile decomposition of the MFMA kernels: a workgroup of eight waves owns a
 // column group of 8 blocks (512 B of each bf16 row; each wave one block,
-// whose K operands stay in its registers) and processes tiles of 16 rows:
-// workgroup (group g, chunk c) takes row tiles c, c + nchunks, ...
+// whose K operands stay in its registers) and processes tiles of 32 rows.
+// The grid has two parts.  The first w1 = ngroups * nchunks workgroups fill
+// the GPU once: workgroup (group g, chunk c) takes row tiles c, c + nchunks,
+// ... below r1.  The rest take the tiles from r1 on, n2 consecutive tiles
+// each; the hardware dispatcher starts them on whichever compute units
+// finish their first-part work first, which evens out the finish times.
 struct MfmaArgs {
   const uint16_t* X;
   int T, d, nb;
@@ -23,6 +27,7 @@ struct MfmaArgs {
   uint8_t* scales;
   float* Y;  // diagnostic output or nullptr
   int ngroups, nchunks;
+  int w1, r1, n2;  // second part of the grid: see above
 };
 
 // Row-segment decomposition of the vector-ALU kernels: a workgroup of four

@@ -18,11 +18,13 @@
 // so that they leave as contiguous 128-byte code segments per row.  Double
 // buffers, one barrier per tile, global loads kept two tiles ahead; all
 // global accesses go through buffer descriptors with wave-uniform cursors
-// advanced by a constant per tile (few scalar instructions per tile).  Output channels are permuted across
-// the MFMA rows so that each lane ends up with 8 consecutive channels of one
+// advanced by a constant per tile (few scalar instructions per tile).
+// Output channels are permuted across the MFMA rows so that each lane ends up with 8 consecutive channels of one
 // token: lane (t = l & 15, q = l >> 4) holds channels 8q .. 8q+7 of token t.
 #include "kq_device.hpp"
 #include "kq_internal.h"
+
+#include <algorithm>
 
 namespace kq {
 
@@ -47,22 +49,44 @@ static_assert(kPPT * kThreads == kPieces, "tile pieces must split evenly over th
 // Output channel held by MFMA row m of half h.
 __device__ __forceinline__ int out_channel(int h, int m) { return 8 * (m >> 2) + 4 * h + (m & 3); }
 
+// The 15 scalars of one block, (l, a, b) of G1 .. G5.
+struct Params15 {
+  float v[15];
+};
+
 // K^T operands of one block for this lane: A[h][s] holds the 8 entries
 // K[8q .. 8q+7][out_channel(h, m)] (q = lane >> 4, m = lane & 15) of term s.
+//
+// From the 15 scalars: one lane builds the five factors in fp64 (G1 .. G5)
+// and stages them in LDS, where the exact path also finds them; every lane then
+// reads the factor entries of its output channel and forms its 8 entries as
+// products in factor order, sharing the partial products of the leading
+// factors (the rounding sequence of each entry is that of kq_build_blocks),
+// rounds them to fp32 and splits them into three bf16 terms.
 template <int KSRC>
-__device__ __forceinline__ void setup_a(bf16x8 A[2][3], int j, const float* __restrict__ P, int pstride,
-                                        const uint16_t* __restrict__ Kbf, int kstride, int lane,
-                                        double* __restrict__ g_lds) {
+__device__ __forceinline__ void setup_a(bf16x8 A[2][3], const Params15& pv, const uint16_t* __restrict__ kblk,
+                                        int lane, double* __restrict__ g_lds) {
   const int m = lane & 15, q = lane >> 4;
   if constexpr (KSRC == KSRC_PARAMS) {
-    const Factors F = factors_f64(P + (int64_t)j * pstride);
-    if (lane == 0) store_factors(F, g_lds);  // for the exact path
+    if (lane == 0) store_factors(factors_f64(pv.v), g_lds);
+    // LDS accesses of one wave complete in issue order; the fence keeps the
+    // compiler from moving the reads above the writes of other lanes.
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int c = out_channel(h, m);
+      // entry [rb][bit of c] of factor k, k = 0 .. 4 (G1 .. G5)
+      auto e = [&](int k, int rb) { return g_lds[4 * k + 2 * rb + ((c >> (4 - k)) & 1)]; };
+      const double p12 = e(0, q >> 1) * e(1, q & 1);
+      const double p3[2] = {p12 * e(2, 0), p12 * e(2, 1)};
+      double p4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) p4[u] = p3[u >> 1] * e(3, u & 1);
+      const double g5[2] = {e(4, 0), e(4, 1)};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float k = k32_entry(F, 8 * q + i, c);
+        const float k = (float)(p4[i >> 1] * g5[i & 1]);
         const __bf16 hi = (__bf16)k;
         const float r1 = k - (float)hi;
         const __bf16 mid = (__bf16)r1;
@@ -73,13 +97,12 @@ __device__ __forceinline__ void setup_a(bf16x8 A[2][3], int j, const float* __re
       }
     }
   } else {
-    const uint16_t* kb = Kbf + (int64_t)j * kstride;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int c = out_channel(h, m);
 #pragma unroll
       for (int s = 0; s < 3; ++s)
-        A[h][s] = *reinterpret_cast<const bf16x8*>(kb + (s * 32 + c) * 32 + 8 * q);
+        A[h][s] = *reinterpret_cast<const bf16x8*>(kblk + (s * 32 + c) * 32 + 8 * q);
     }
   }
 }
@@ -93,15 +116,42 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(MfmaArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int g = wg % a.ngroups, c = wg / a.ngroups;
+  const int ntile_rows = (a.T + kRows - 1) / kRows;
+  // Work of this workgroup: column group g, nsteps row tiles starting at row
+  // row_first, step_rows apart, all below row_end.
+  int g, row_first, step_rows, nsteps, row_end;
+  if ((int)blockIdx.x < a.w1) {
+    const int wg = xcd_remap(blockIdx.x, a.w1);
+    const int c = wg / a.ngroups;
+    const int lim = min(a.r1, ntile_rows);
+    g = wg % a.ngroups;
+    nsteps = c < lim ? (lim - 1 - c) / a.nchunks + 1 : 0;
+    row_first = kRows * c;
+    step_rows = kRows * a.nchunks;
+    row_end = min(a.T, kRows * lim);
+  } else {
+    const int wg = xcd_remap((int)blockIdx.x - a.w1, (int)gridDim.x - a.w1);
+    const int t0 = a.r1 + (wg / a.ngroups) * a.n2;
+    g = wg % a.ngroups;
+    nsteps = max(0, min(a.n2, ntile_rows - t0));
+    row_first = kRows * t0;
+    step_rows = kRows;
+    row_end = min(a.T, kRows * (t0 + nsteps));
+  }
   const int jg = kCB * g;
   const int nvalid = min(kCB, a.nb - jg);
   const int64_t d = a.d;
-  const int ntile_rows = (a.T + kRows - 1) / kRows;
-  const int nsteps = c < ntile_rows ? (ntile_rows - 1 - c) / a.nchunks + 1 : 0;
 
   const bool mine = wv < nvalid;  // this wave's block exists
+  // The block's scalars are requested first, and unconditionally (a clamped
+  // block for waves without one), so that no wait for them lands in front of
+  // the first X loads.
+  Params15 pv;
+  if constexpr (KSRC == KSRC_PARAMS) {
+    const float* p = a.P + (int64_t)min(jg + wv, a.nb - 1) * a.pstride;
+#pragma unroll
+    for (int i = 0; i < 15; ++i) pv.v[i] = p[i];
+  }
   bf16x8 A[2][3];                 // K^T operands: [output half][term hi, mid, lo]
 
   uint32_t xoff[kPPT];
@@ -130,18 +180,17 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(MfmaArgs a) {
   u32x4 pre[kAhead][kPPT];
   // Wave-uniform cursors, advanced by a constant per tile: the next tile to
   // load and the next tile to write out.  `left` counts the rows from a
-  // cursor to the end of the matrix (negative past it); range sizes are
-  // clamped to one tile, so rows past the end read zeros / drop stores.
-  const int step_rows = kRows * a.nchunks;
+  // cursor to row_end (negative past it); range sizes are clamped to one
+  // tile, so rows past the end read zeros / drop stores, and the loads
+  // issued ahead of the last tile fetch nothing.
   const int xrow_bytes = 2 * a.d, crow_bytes = a.d >> 1, srow_bytes = a.nb;
-  const int row_first = kRows * c;
   auto rows_in = [](int left) { return left <= 0 ? 0 : (left >= kRows ? kRows : left); };
 
-  int lleft = a.T - row_first;
+  int lleft = row_end - row_first;
   const uint8_t* lx = reinterpret_cast<const uint8_t*>(a.X) + (int64_t)row_first * xrow_bytes;
   const int64_t lstep = (int64_t)step_rows * xrow_bytes;
   auto gload_next = [&](u32x4 (&r)[kPPT]) {
-    const auto rx = rsrc(lx, rows_in(lleft) * xrow_bytes);
+    const auto rx = rsrc_uniform(lx, rows_in(lleft) * xrow_bytes);
 #pragma unroll
     for (int k = 0; k < kPPT; ++k) r[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[k], 0, kNT);
     lleft -= step_rows;
@@ -151,14 +200,14 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(MfmaArgs a) {
 #pragma unroll
     for (int k = 0; k < kPPT; ++k) *reinterpret_cast<u32x4*>(&lds_in[buf][lin[k]]) = r[k];
   };
-  int sleft = a.T - row_first;
+  int sleft = row_end - row_first;
   uint8_t* sc = a.codes + (int64_t)row_first * crow_bytes;
   uint8_t* ss = a.scales + (int64_t)row_first * srow_bytes;
   const int64_t cstep = (int64_t)step_rows * crow_bytes, sstep = (int64_t)step_rows * srow_bytes;
   auto gstore_next = [&](int buf) {
     const int n = rows_in(sleft);
-    const auto rc = rsrc(sc, n * crow_bytes);
-    const auto rs = rsrc(ss, n * srow_bytes);
+    const auto rc = rsrc_uniform(sc, n * crow_bytes);
+    const auto rs = rsrc_uniform(ss, n * srow_bytes);
 #pragma unroll
     for (int k = 0; k < kOPT; ++k) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(&lds_out[buf][lout[k]]);
@@ -234,7 +283,7 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(MfmaArgs a) {
   // Loads of the first kAhead tiles go out before the K setup, which overlaps them.
 #pragma unroll
   for (int k = 0; k < kAhead; ++k) gload_next(pre[k]);
-  if (mine) setup_a<KSRC>(A, jg + wv, a.P, a.pstride, a.Kbf, a.kstride, lane, lds_g[wv]);
+  if (mine) setup_a<KSRC>(A, pv, KSRC == KSRC_SPLIT ? a.Kbf + (int64_t)(jg + wv) * a.kstride : nullptr, lane, lds_g[wv]);
 
   // Per tile s: stage tile s into LDS, fetch tile s + kAhead, barrier, write
   // out tile s - 1, compute tile s.  Every memory instruction is issued
@@ -275,10 +324,22 @@ hipError_t launch_mfma(int ksrc, bool store_y, const MfmaArgs& args, hipStream_t
   else
     fn = store_y ? (const void*)&mfma_kernel<KSRC_SPLIT, true> : (const void*)&mfma_kernel<KSRC_SPLIT, false>;
   MfmaArgs a = args;
+  const int nt = (a.T + kRows - 1) / kRows;
   a.ngroups = (a.nb + kCB - 1) / kCB;
-  a.nchunks = chunks_one_round(fn, kThreads, a.ngroups, (a.T + kRows - 1) / kRows);
+  a.nchunks = chunks_one_round(fn, kThreads, a.ngroups, nt);
+  // Second part of the grid (tiles from r1 on, n2 per workgroup), sized by
+  // the tiles a first-part workgroup would otherwise take (measured on
+  // MI355X: finish times of equal first-part workgroups spread by up to a
+  // fifth of the kernel, with the slow ones tied to address ranges).
+  const int per = (nt + a.nchunks - 1) / a.nchunks;
+  const int tail_pct = per >= 24 ? 18 : (per >= 8 ? 12 : 6);
+  a.n2 = per >= 24 ? 6 : (per >= 8 ? 4 : 2);
+  const int n1 = std::max(1, (int)((int64_t)nt * (100 - tail_pct) / (100 * (int64_t)a.nchunks)));
+  a.r1 = (int)std::min<int64_t>(nt, (int64_t)n1 * a.nchunks);
+  a.w1 = a.ngroups * a.nchunks;
+  const int64_t w2 = (int64_t)a.ngroups * ((nt - a.r1 + a.n2 - 1) / a.n2);
   void* kargs[] = {&a};
-  return hipLaunchKernel(fn, dim3(a.ngroups * a.nchunks), dim3(kThreads), kargs, 0, stream);
+  return hipLaunchKernel(fn, dim3((unsigned)(a.w1 + w2)), dim3(kThreads), kargs, 0, stream);
 }
 
 }  // namespace kq
