@@ -280,10 +280,13 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(MfmaArgs a) {
     }
   };
 
-  // Loads of the first kAhead tiles go out before the K setup, which overlaps them.
-#pragma unroll
-  for (int k = 0; k < kAhead; ++k) gload_next(pre[k]);
+  // The first tile's loads go out before the K setup, which overlaps them;
+  // the loads of the next tiles follow the setup, so that at the start of the
+  // kernel (every workgroup issuing at once) the first tiles arrive early.
+  gload_next(pre[0]);
   if (mine) setup_a<KSRC>(A, pv, KSRC == KSRC_SPLIT ? a.Kbf + (int64_t)(jg + wv) * a.kstride : nullptr, lane, lds_g[wv]);
+#pragma unroll
+  for (int k = 1; k < kAhead; ++k) gload_next(pre[k]);
 
   // Per tile s: stage tile s into LDS, fetch tile s + kAhead, barrier, write
   // out tile s - 1, compute tile s.  Every memory instruction is issued
