@@ -61,6 +61,10 @@ def lib():
         L.kqo_fwht32.argtypes = [vp]
         L.kqo_det.argtypes = [vp, ci]
         L.kqo_det.restype = d
+        L.kqo_row_stats.argtypes = [vp, i64, i64, d, vp]
+        L.kqo_row_stats.restype = ci
+        L.kqo_adaln_rows.argtypes = [vp, i64, i64, vp, vp, vp, i64, vp]
+        L.kqo_adaln_rows.restype = ci
         _lib = L
     return _lib
 
@@ -200,6 +204,33 @@ def quantize_rows(front: int, X: np.ndarray, P=None, pstride: int = 15, m=None, 
     out = {"codes": codes, "scales": scales}
     if want_y:
         out["y32"], out["yhat"] = y32, yhat
+    return out
+
+
+def row_stats(X: np.ndarray, eps: float = 1e-6) -> np.ndarray:
+    """LayerNorm statistics float32 [T, 2] = (mean, rstd) per row (fp64 sums, channel order)."""
+    X = np.ascontiguousarray(X, dtype=np.uint16)
+    T, d = X.shape
+    st = np.zeros((T, 2), dtype=np.float32)
+    if lib().kqo_row_stats(X.ctypes.data, T, d, float(eps), st.ctypes.data) != 0:
+        raise ValueError("oracle rejected its arguments")
+    return st
+
+
+def adaln_rows(X: np.ndarray, stats=None, mscale=None, mshift=None, tokens_per_sample: int | None = None) -> np.ndarray:
+    """The modulated activation as bf16 bits [T, d] (fp32 steps: centre, scale by rstd,
+    times (1 + scale), plus shift; then round to bf16)."""
+    X = np.ascontiguousarray(X, dtype=np.uint16)
+    T, d = X.shape
+    tps = T if tokens_per_sample is None else int(tokens_per_sample)
+    cvt = lambda a: None if a is None else np.ascontiguousarray(a, dtype=np.float32)
+    st, ms, mh = cvt(stats), cvt(mscale), cvt(mshift)
+    out = np.zeros((T, d), dtype=np.uint16)
+    rc = lib().kqo_adaln_rows(X.ctypes.data, T, d, None if st is None else st.ctypes.data,
+                              None if ms is None else ms.ctypes.data, None if mh is None else mh.ctypes.data,
+                              max(tps, 1), out.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
     return out
 
 

@@ -301,3 +301,49 @@ int kqo_quantize_f32_rows(const float* Y, int64_t n, int64_t d, uint8_t* codes, 
     for (int64_t j = 0; j < nb; ++j) kqo_quantize_block(Y + t * d + 32 * j, codes + t * (d / 2) + 16 * j, scales + t * nb + j);
   return 0;
 }
+
+/*
+ * LayerNorm statistics (see kq_oracle.h): two passes over the row in fp64,
+ * channel order, then one fp64 division and square root for rstd.
+ */
+int kqo_row_stats(const uint16_t* X, int64_t T, int64_t d, double eps, float* stats) {
+  if (!X || !stats || T < 0 || d <= 0 || !(eps >= 0.0)) return 1;
+  for (int64_t t = 0; t < T; ++t) {
+    const uint16_t* x = X + t * d;
+    double s = 0.0;
+    for (int64_t c = 0; c < d; ++c) s += bf16_to_f64(x[c]);
+    const double mean = s / (double)d;
+    double q = 0.0;
+    for (int64_t c = 0; c < d; ++c) {
+      const double u = bf16_to_f64(x[c]) - mean;
+      q += u * u;
+    }
+    const double var = q / (double)d;
+    stats[2 * t] = (float)mean;
+    stats[2 * t + 1] = (float)(1.0 / sqrt(var + eps));
+  }
+  return 0;
+}
+
+/* The modulated activation (see kq_oracle.h): fp32 steps in the stated order. */
+int kqo_adaln_rows(const uint16_t* X, int64_t T, int64_t d, const float* stats, const float* mscale,
+                   const float* mshift, int64_t tokens_per_sample, uint16_t* Xmod) {
+  if (!X || !Xmod || T < 0 || d <= 0 || tokens_per_sample <= 0) return 1;
+  for (int64_t t = 0; t < T; ++t) {
+    const int64_t s = t / tokens_per_sample;
+    for (int64_t c = 0; c < d; ++c) {
+      float v = bf16_to_f32(X[t * d + c]);
+      if (stats) {
+        const float centred = v - stats[2 * t];
+        v = centred * stats[2 * t + 1];
+      }
+      if (mscale) {
+        const float one_plus = 1.0f + mscale[s * d + c];
+        v = v * one_plus;
+      }
+      if (mshift) v = v + mshift[s * d + c];
+      Xmod[t * d + c] = f32_to_bf16_rne(v);
+    }
+  }
+  return 0;
+}

@@ -72,6 +72,32 @@ int kqo_quantize_rows(int front, const uint16_t* X, int64_t T, int64_t d, const 
 /* MXFP4 of given fp32 values Y[n][d] (steps after the transform only). */
 int kqo_quantize_f32_rows(const float* Y, int64_t n, int64_t d, uint8_t* codes, uint8_t* scales);
 
+/*
+ * Producer step in front of the quantizer (AdaLN: the Pith review's summary
+ * gives AdaLN as the reason the transform must run online, and its ledger
+ * lists LayerNorm / AdaLN as normalisations that do not commute with it; the
+ * handbook page "Quantization: where diffusion differs from an LLM" describes
+ * AdaLN as timestep-dependent per-channel scales and shifts).
+ *
+ * kqo_row_stats: LayerNorm statistics without affine parameters, per row:
+ *   mean = (sum_c x) / d, var = (sum_c (x - mean)^2) / d, both summed in fp64
+ *   in channel order; rstd = 1 / sqrt(var + eps) in fp64; stored as the fp32
+ *   pair (mean, rstd) at stats[2t], stats[2t+1].  Returns 0, or 1 on bad args.
+ */
+int kqo_row_stats(const uint16_t* X, int64_t T, int64_t d, double eps, float* stats);
+/*
+ * kqo_adaln_rows: the modulated activation, per element in fp32, one IEEE
+ * operation each and in this order (no contraction):
+ *   v = x                                  (bf16 -> fp32, exact)
+ *   v = (v - mean_t) * rstd_t              if stats != NULL
+ *   v = v * (1 + scale[s][c])              if mscale != NULL; (1 + scale) is one fp32 add
+ *   v = v + shift[s][c]                    if mshift != NULL
+ * with s = t / tokens_per_sample (scale, shift: fp32 [n_samples][d]), then
+ * rounded to bf16 (nearest even) into Xmod [T][d].  Returns 0, or 1.
+ */
+int kqo_adaln_rows(const uint16_t* X, int64_t T, int64_t d, const float* stats, const float* mscale,
+                   const float* mshift, int64_t tokens_per_sample, uint16_t* Xmod);
+
 /* Fast Walsh-Hadamard transform of 32 values in place (natural order, unnormalized). */
 void kqo_fwht32(double v[32]);
 /* Determinant of an n x n fp64 matrix by LU with partial pivoting. */
