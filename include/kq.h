@@ -104,7 +104,7 @@ typedef enum {
 typedef enum { KQ_FRONT_KRON = 0, KQ_FRONT_PLAIN = 1, KQ_FRONT_SMOOTH = 2, KQ_FRONT_HADAMARD = 3 } kq_front;
 
 /* ABI version of this header (bumped on any signature or layout change). */
-#define KQ_ABI_VERSION 1
+#define KQ_ABI_VERSION 2
 int kq_abi_version(void);
 
 /* Static, never-NULL description of a status code. */
@@ -183,6 +183,47 @@ kq_status kq_transform_f32(int front, const uint16_t* X, int64_t tokens, int64_t
                            int64_t params_block_stride, const uint16_t* K_bf16, kq_variant variant,
                            const float* ch_mult, float* Y, uint8_t* out_codes, uint8_t* out_scales,
                            hipStream_t stream);
+
+/*
+ * LayerNorm statistics per row, for the AdaLN producer step below (the
+ * normalisation without affine parameters that precedes a DiT linear
+ * layer's AdaLN modulation; the Pith review's summary gives AdaLN as the
+ * reason the transform runs online, its ledger lists LayerNorm / AdaLN as
+ * normalisations that do not commute with it).  For each row t:
+ *   mean = sum_c x / d, var = sum_c (x - mean)^2 / d   (fp64 sums),
+ *   rstd = 1 / sqrt(var + eps)                         (fp64),
+ * stored as fp32 row_stats[2t] = mean, row_stats[2t+1] = rstd.  The fp64
+ * summation order is unspecified: results can differ from a sequential
+ * evaluation by one fp32 ulp, rarely.  Errors as above; eps < 0 or not finite
+ * -> KQ_ERR_SHAPE; X 16-byte and row_stats 8-byte aligned.
+ */
+kq_status kq_row_stats(const uint16_t* X, int64_t tokens, int64_t d, float eps, float* row_stats,
+                       hipStream_t stream);
+
+/*
+ * The quantizer with the AdaLN producer step fused in front of the transform
+ * (one read of X instead of a modulation kernel's read + write followed by
+ * the quantizer's read).  Each element, in fp32, one IEEE operation each and
+ * in this order (no contraction):
+ *   v = x;
+ *   v = (v - mean_t) * rstd_t                 if row_stats != NULL ([tokens][2], above);
+ *   v = v * (1 + mod_scale[s][c])             if mod_scale != NULL;
+ *   v = v + mod_shift[s][c]                   if mod_shift != NULL;
+ * with s = t / tokens_per_sample and mod_scale, mod_shift fp32
+ * [ceil(tokens / tokens_per_sample)][d]; v is rounded to bf16 (nearest even)
+ * and then transformed and quantized exactly as kq_quantize_ex would
+ * transform and quantize that bf16 matrix (the handbook page "Quantization:
+ * where diffusion differs from an LLM" describes AdaLN as timestep-dependent
+ * per-channel scales and shifts; the form v (1 + scale) + shift is the DiT
+ * one).  tokens_per_sample must be a multiple of 32 or at least tokens
+ * (KQ_ERR_SHAPE otherwise).  Variants: KQ_AUTO, KQ_MFMA_OTF, KQ_MFMA_DENSE
+ * with the same inputs as kq_quantize_ex; KQ_BUTTERFLY -> KQ_ERR_VARIANT.
+ * row_stats must be 8-byte aligned, mod_scale / mod_shift 4-byte aligned.
+ */
+kq_status kq_quantize_adaln(const uint16_t* X, int64_t tokens, int64_t d, const float* row_stats,
+                            const float* mod_scale, const float* mod_shift, int64_t tokens_per_sample,
+                            const float* K_params, int64_t params_block_stride, const uint16_t* K_bf16,
+                            kq_variant variant, uint8_t* out_codes, uint8_t* out_scales, hipStream_t stream);
 
 #ifdef __cplusplus
 }

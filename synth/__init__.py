@@ -46,6 +46,8 @@ def _load():
         lib.synth_uniform.restype = dbl
         lib.synth_normal.argtypes = [u64, u64, u64]
         lib.synth_normal.restype = dbl
+        lib.synth_adaln.argtypes = [vp, vp, i64, i64, u64, u64, dbl, dbl, dbl]
+        lib.synth_adaln.restype = ci
         _lib = lib
     return _lib
 
@@ -160,6 +162,18 @@ def random_matrix(T: int, d: int, seed: int, kind: int = BASE_NORMAL, n_outliers
                   token_sigma: float = 0.5, zero_frac: float = 0.0, matrix_id: int = 7) -> np.ndarray:
     spec = MatrixSpec("adhoc", T, d, seed, matrix_id, kind, n_outliers, mult, token_sigma, zero_frac)
     return matrix(spec)
+
+
+def adaln_vectors(n_samples: int, d: int, seed: int, matrix_id: int = 11, sigma: float = 0.5,
+                  amplified_frac: float = 0.01, amp: float = 20.0):
+    """AdaLN (scale, shift), float32 [n_samples, d] each: N(0, sigma) values, and a
+    fixed 1% of channels whose scale is raised by ``amp`` (amplified channels)."""
+    lib = _load()
+    sc = np.empty((n_samples, d), dtype=np.float32)
+    sh = np.empty((n_samples, d), dtype=np.float32)
+    if lib.synth_adaln(sc.ctypes.data, sh.ctypes.data, n_samples, d, seed, matrix_id, sigma, amplified_frac, amp) != 0:
+        raise RuntimeError("synth_adaln failed")
+    return sc, sh
 
 
 def smooth_mult(X: np.ndarray) -> np.ndarray:

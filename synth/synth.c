@@ -207,3 +207,36 @@ int synth_smooth_mult(const uint16_t* X, int64_t T, int64_t d, float* m) {
   free(amax);
   return 0;
 }
+
+/*
+ * AdaLN modulation vectors, fp32 [n_samples][d] each: scale = sigma * N(0,1)
+ * with every channel in `amplified` (a uniform sample of round(frac * d)
+ * channels, the same for every sample) raised by `amp`, and shift =
+ * sigma * N(0,1).  AdaLN multiplies timestep-dependent scales onto the
+ * activations and amplifies a few channels many times over (handbook page
+ * "Quantization: where diffusion differs from an LLM", differences list).
+ */
+int synth_adaln(float* scale, float* shift, int64_t n_samples, int64_t d, uint64_t seed, uint64_t matrix_id,
+                double sigma, double frac, double amp) {
+  if (!scale || !shift || n_samples <= 0 || d <= 0) return 1;
+  const uint64_t base = matrix_id << 8;
+  for (int64_t i = 0; i < n_samples * d; ++i) {
+    scale[i] = (float)(sigma * synth_normal(seed, base | 20u, (uint64_t)i));
+    shift[i] = (float)(sigma * synth_normal(seed, base | 21u, (uint64_t)i));
+  }
+  const int64_t k = (int64_t)(frac * (double)d + 0.5);
+  if (k <= 0) return 0;
+  int64_t* idx = (int64_t*)malloc((size_t)d * sizeof(int64_t));
+  if (!idx) return 2;
+  for (int64_t c = 0; c < d; ++c) idx[c] = c;
+  for (int64_t c = 0; c < k && c < d; ++c) {  // partial Fisher-Yates
+    const int64_t r = c + (int64_t)(synth_uniform(seed, base | 22u, (uint64_t)c) * (double)(d - c));
+    const int64_t tmp = idx[c];
+    idx[c] = idx[r < d ? r : d - 1];
+    idx[r < d ? r : d - 1] = tmp;
+  }
+  for (int64_t s = 0; s < n_samples; ++s)
+    for (int64_t c = 0; c < k && c < d; ++c) scale[s * d + idx[c]] += (float)amp;
+  free(idx);
+  return 0;
+}

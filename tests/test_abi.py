@@ -33,6 +33,8 @@ def lib():
     L.kq_smooth_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp]
     L.kq_hadamard_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
     L.kq_transform_f32.argtypes = [ci, vp, i64, i64, vp, i64, vp, ci, vp, vp, vp, vp, vp]
+    L.kq_row_stats.argtypes = [vp, i64, i64, ctypes.c_float, vp, vp]
+    L.kq_quantize_adaln.argtypes = [vp, i64, i64, vp, vp, vp, i64, vp, i64, vp, ci, vp, vp, vp]
     L.kq_status_str.restype = ctypes.c_char_p
     return L
 
@@ -40,7 +42,8 @@ def lib():
 def test_header_declares_expected_entry_points():
     names = declared()
     for n in ("kq_build_blocks", "kq_quantize", "kq_quantize_ex", "kq_mx_quantize", "kq_smooth_quantize",
-              "kq_hadamard_quantize", "kq_transform_f32", "kq_status_str", "kq_abi_version"):
+              "kq_hadamard_quantize", "kq_transform_f32", "kq_status_str", "kq_abi_version", "kq_row_stats",
+              "kq_quantize_adaln"):
         assert n in names
 
 
@@ -131,3 +134,39 @@ def test_binding_raises_without_gpu_tensors():
     X = torch.zeros((4, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         kq.kq_mx_quantize(X, X, X)
+
+
+E = 0x500000
+F = 0x600000
+G = 0x700000
+
+
+def test_row_stats_argument_checks(lib):
+    assert lib.kq_row_stats(A, 4, 48, 1e-6, B, None) == KQ_ERR_SHAPE
+    assert lib.kq_row_stats(A, 4, 64, -1.0, B, None) == KQ_ERR_SHAPE
+    assert lib.kq_row_stats(A, 4, 64, float("nan"), B, None) == KQ_ERR_SHAPE
+    assert lib.kq_row_stats(A, 0, 64, 1e-6, None, None) == KQ_OK
+    assert lib.kq_row_stats(None, 4, 64, 1e-6, B, None) == KQ_ERR_NULL
+    assert lib.kq_row_stats(A, 4, 64, 1e-6, None, None) == KQ_ERR_NULL
+    assert lib.kq_row_stats(A + 2, 4, 64, 1e-6, B, None) == KQ_ERR_ALIGN
+    assert lib.kq_row_stats(A, 4, 64, 1e-6, B + 4, None) == KQ_ERR_ALIGN
+    assert lib.kq_row_stats(A, 4, 64, 1e-6, A + 8, None) == KQ_ERR_ALIAS
+
+
+def test_quantize_adaln_argument_checks(lib):
+    q = lib.kq_quantize_adaln
+    # tokens_per_sample must be positive and a multiple of 32 unless it covers every row
+    assert q(A, 100, 64, B, C, D, 0, E, 15, None, 0, F, G, None) == KQ_ERR_SHAPE
+    assert q(A, 100, 64, B, C, D, 40, E, 15, None, 0, F, G, None) == KQ_ERR_SHAPE
+    assert q(A, 100, 64, B, C, D, 64, E, 7, None, 0, F, G, None) == KQ_ERR_SHAPE
+    assert q(A, 100, 64, B, C, D, 64, E, 15, None, 3, F, G, None) == KQ_ERR_VARIANT
+    assert q(A, 100, 64, B, C, D, 64, E, 15, None, 9, F, G, None) == KQ_ERR_VARIANT
+    assert q(A, 0, 64, None, None, None, 64, None, 15, None, 0, None, None, None) == KQ_OK
+    assert q(A, 100, 64, B, C, D, 64, None, 15, None, 0, F, G, None) == KQ_ERR_VARIANT
+    assert q(A, 100, 64, B, C, D, 64, E, 15, None, 1, F, G, None) == KQ_ERR_VARIANT
+    assert q(None, 100, 64, B, C, D, 64, E, 15, None, 0, F, G, None) == KQ_ERR_NULL
+    assert q(A, 100, 64, B + 4, C, D, 64, E, 15, None, 0, F, G, None) == KQ_ERR_ALIGN
+    assert q(A, 100, 64, B, C + 2, D, 64, E, 15, None, 0, F, G, None) == KQ_ERR_ALIGN
+    # an output overlapping the statistics or a modulation vector
+    assert q(A, 100, 64, B, C, D, 64, E, 15, None, 0, B + 64, G, None) == KQ_ERR_ALIAS
+    assert q(A, 100, 64, B, C, D, 64, E, 15, None, 0, F, D + 16, None) == KQ_ERR_ALIAS

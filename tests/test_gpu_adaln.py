@@ -1,0 +1,185 @@
+"""Parity of the fused AdaLN producer step + quantizer, and of the LayerNorm
+row statistics, with the CPU oracle, on an MI355X (through the C ABI).
+
+The fused entry point must produce exactly what the quantizer produces on the
+bf16 matrix the oracle's producer step writes: scales bit-exact, codes exact
+except at rounding ties inside the transform's error bound, and bit-identical
+to kq_quantize_ex on the oracle's modulated matrix (the GPU rounds to the same
+bf16 values and then runs the same transform).  Row statistics within one fp32
+ulp of the oracle's sequential fp64 evaluation.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from oracle.compare import compare
+
+kq = pytest.importorskip("w4a4_diffusion_transformer_amd")
+
+pytestmark = pytest.mark.gpu
+
+THREADS = max(1, min(16, os.cpu_count() or 1))
+REPORT = os.environ.get("KQ_PARITY_REPORT")
+EPS = float(np.float32(1e-6))
+
+
+def record(name: str, rep) -> None:
+    print(f"{name}: {rep}", flush=True)
+    if REPORT:
+        with open(REPORT, "a") as f:
+            f.write(f"{name}: {rep}\n")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    kq.lib()
+    yield
+
+
+def dev(a):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def ulp_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    ia = a.view(np.int32).astype(np.int64)
+    ib = b.view(np.int32).astype(np.int64)
+    return np.abs(ia - ib)
+
+
+def inputs(T, d, tps, seed, kind=synth.BASE_NORMAL):
+    X = synth.random_matrix(T, d, seed, kind=kind, n_outliers=max(1, d // 100), mult=50.0, token_sigma=0.5)
+    P = synth.random_params(d // 32, seed=seed + 100)
+    ns = (T + tps - 1) // tps
+    sc, sh = synth.adaln_vectors(ns, d, seed=seed + 200)
+    st = oracle.row_stats(X, eps=EPS)
+    return X, P, st, sc, sh
+
+
+def run_fused(X, P, st, sc, sh, tps, variant):
+    Xd = dev(X)
+    codes, scales = kq.alloc_outputs(Xd)
+    Pd = dev(P)
+    Kbf = None
+    if variant == kq.KQ_MFMA_DENSE:
+        Kbf = torch.empty((P.shape[0], 3, 32, 32), dtype=torch.int16, device="cuda:0")
+        kq.kq_build_blocks(Pd, P.shape[0], None, Kbf, 3)
+        Pd = None
+    kq.kq_quantize_adaln(Xd, dev(st), dev(sc), dev(sh), tps, Pd, codes, scales, 15, Kbf, variant)
+    torch.cuda.synchronize()
+    return host(codes), host(scales)
+
+
+def run_plain_kron(Xmod, P):
+    Xd = dev(Xmod)
+    codes, scales = kq.alloc_outputs(Xd)
+    kq.kq_quantize_ex(Xd, dev(P), 15, None, kq.KQ_MFMA_OTF, codes, scales)
+    torch.cuda.synchronize()
+    return host(codes), host(scales)
+
+
+def check(name, X, P, st, sc, sh, tps, variant, against_unfused=True):
+    codes, scales = run_fused(X, P, st, sc, sh, tps, variant)
+    Xmod = oracle.adaln_rows(X, st, sc, sh, tokens_per_sample=tps)
+    ref = oracle.quantize_rows(oracle.KRON, Xmod, P, threads=THREADS)
+
+    def yh(rows):
+        o = oracle.quantize_rows(oracle.KRON, Xmod[rows], P, want_y=True)
+        return o["yhat"], o["y32"]
+
+    rep = compare(codes, scales, ref["codes"], ref["scales"], yh)
+    record(name, rep)
+    assert rep.ok(), f"{name}: {rep}"
+    if against_unfused and variant == kq.KQ_MFMA_OTF:
+        c2, s2 = run_plain_kron(Xmod, P)
+        np.testing.assert_array_equal(scales, s2)
+        np.testing.assert_array_equal(codes, c2)
+
+
+# ---------------------------------------------------------------- row statistics
+
+
+@pytest.mark.parametrize("T,d", [(1, 32), (7, 64), (33, 1152), (300, 3072), (64, 12288), (1000, 160)])
+def test_row_stats(T, d):
+    X = synth.random_matrix(T, d, seed=T + d, n_outliers=max(1, d // 64), mult=80.0)
+    st = torch.empty((T, 2), dtype=torch.float32, device="cuda:0")
+    kq.kq_row_stats(dev(X), EPS, st)
+    torch.cuda.synchronize()
+    ref = oracle.row_stats(X, eps=EPS)
+    got = host(st)
+    u = ulp_diff(got, ref)
+    assert u.max() <= 1, f"max ulp {u.max()}"
+    assert (u == 0).mean() >= 0.99
+
+
+def test_row_stats_constant_and_zero_rows():
+    X = np.zeros((4, 64), dtype=np.uint16)
+    X[1] = synth.f32_to_bf16(np.full(64, 3.0, np.float32))
+    st = torch.empty((4, 2), dtype=torch.float32, device="cuda:0")
+    kq.kq_row_stats(dev(X), EPS, st)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(st), oracle.row_stats(X, eps=EPS))
+
+
+# ---------------------------------------------------------------- fused producer step
+
+
+MODES = {
+    "all": (True, True, True),
+    "stats_only": (True, False, False),
+    "modulation_only": (False, True, True),
+    "scale_only": (False, True, False),
+}
+
+
+@pytest.mark.parametrize("mode", list(MODES))
+@pytest.mark.parametrize("T,d,tps", [(64, 1152, 32), (300, 3072, 300), (257, 2240, 128), (96, 5600, 64)])
+@pytest.mark.parametrize("variant", [2, 1])
+def test_fused_small(T, d, tps, mode, variant):
+    X, P, st, sc, sh = inputs(T, d, tps, seed=T * 7 + d)
+    us, usc, ush = MODES[mode]
+    check(f"adaln {T}x{d} tps{tps} {mode} v{variant}", X, P, st if us else None, sc if usc else None,
+          sh if ush else None, tps, variant)
+
+
+def test_fused_without_producer_inputs_equals_quantizer():
+    X, P, _, _, _ = inputs(200, 1152, 200, seed=5)
+    codes, scales = run_fused(X, P, None, None, None, 200, kq.KQ_MFMA_OTF)
+    c2, s2 = run_plain_kron(X, P)
+    np.testing.assert_array_equal(codes, c2)
+    np.testing.assert_array_equal(scales, s2)
+
+
+@pytest.mark.parametrize("name,T,d,tps,kind", [
+    ("flux_x1", 4608, 3072, 4608, synth.BASE_NORMAL),        # FLUX.1-schnell width, one sample of 4096 + 512 tokens
+    ("pixart_x1", 8192, 1152, 4096, synth.BASE_NORMAL),      # PixArt-Sigma width, batch 2 x 4096 tokens
+    ("sana_x1", 4096, 2240, 1024, synth.BASE_NORMAL),        # SANA width, batch 4 x 1024 tokens
+])
+def test_fused_full_workloads(name, T, d, tps, kind):
+    X, P, st, sc, sh = inputs(T, d, tps, seed={"flux_x1": 31, "pixart_x1": 32, "sana_x1": 33}[name], kind=kind)
+    check(f"adaln {name}", X, P, st, sc, sh, tps, kq.KQ_MFMA_OTF)
+
+
+def test_fused_error_codes():
+    X, P, st, sc, sh = inputs(100, 64, 64, seed=9)
+    Xd = dev(X)
+    codes, scales = kq.alloc_outputs(Xd)
+    with pytest.raises(kq.KQError) as e:
+        kq.kq_quantize_adaln(Xd, dev(st), dev(sc), dev(sh), 40, dev(P), codes, scales)
+    assert e.value.status == 2
+    with pytest.raises(kq.KQError) as e:
+        kq.kq_quantize_adaln(Xd, dev(st), dev(sc), dev(sh), 64, dev(P), codes, scales, 15, None, kq.KQ_BUTTERFLY)
+    assert e.value.status == 4

@@ -19,7 +19,7 @@ __all__ = [
     "KQ_FRONT_KRON", "KQ_FRONT_PLAIN", "KQ_FRONT_SMOOTH", "KQ_FRONT_HADAMARD",
     "lib", "kq_abi_version", "kq_status_str", "kq_build_blocks", "kq_quantize", "kq_quantize_ex",
     "kq_mx_quantize", "kq_smooth_quantize", "kq_hadamard_quantize", "kq_transform_f32",
-    "alloc_outputs", "LIB_PATH", "kq_auto_variant", "variant_name",
+    "alloc_outputs", "LIB_PATH", "kq_auto_variant", "variant_name", "kq_row_stats", "kq_quantize_adaln",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkq.so")
@@ -58,8 +58,10 @@ def lib() -> ctypes.CDLL:
         L.kq_transform_f32.argtypes = [ci, vp, i64, i64, vp, i64, vp, ci, vp, vp, vp, vp, vp]
         L.kq_auto_variant.argtypes = [i64, i64, ci, ci]
         L.kq_auto_variant.restype = ci
+        L.kq_row_stats.argtypes = [vp, i64, i64, ctypes.c_float, vp, vp]
+        L.kq_quantize_adaln.argtypes = [vp, i64, i64, vp, vp, vp, i64, vp, i64, vp, ci, vp, vp, vp]
         for name in ("kq_build_blocks", "kq_quantize", "kq_quantize_ex", "kq_mx_quantize", "kq_smooth_quantize",
-                     "kq_hadamard_quantize", "kq_transform_f32"):
+                     "kq_hadamard_quantize", "kq_transform_f32", "kq_row_stats", "kq_quantize_adaln"):
             getattr(L, name).restype = ci
         _lib = L
     return _lib
@@ -185,3 +187,23 @@ def kq_transform_f32(front: int, X, K_params=None, params_block_stride: int = 15
                                   _ptr(out_codes, "out_codes", _U8), _ptr(out_scales, "out_scales", _U8),
                                   _stream(stream)), "kq_transform_f32")
     return Y, out_codes, out_scales
+
+
+def kq_row_stats(X, eps: float, row_stats, stream=None):
+    """LayerNorm (mean, rstd) per row into row_stats (float32 [tokens, 2])."""
+    T, d = _shape(X)
+    _check(lib().kq_row_stats(_ptr(X, "X", _BF16), T, d, float(eps), _ptr(row_stats, "row_stats", _F32),
+                              _stream(stream)), "kq_row_stats")
+    return row_stats
+
+
+def kq_quantize_adaln(X, row_stats, mod_scale, mod_shift, tokens_per_sample: int, K_params, out_codes, out_scales,
+                      params_block_stride: int = 15, K_bf16=None, variant: int = KQ_AUTO, stream=None):
+    """Fused LayerNorm-normalise + AdaLN-modulate + transform + MXFP4 (any of the first three inputs may be None)."""
+    T, d = _shape(X)
+    _check(lib().kq_quantize_adaln(_ptr(X, "X", _BF16), T, d, _ptr(row_stats, "row_stats", _F32),
+                                   _ptr(mod_scale, "mod_scale", _F32), _ptr(mod_shift, "mod_shift", _F32),
+                                   int(tokens_per_sample), _ptr(K_params, "K_params", _F32), params_block_stride,
+                                   _ptr(K_bf16, "K_bf16", _BF16), int(variant), _ptr(out_codes, "out_codes", _U8),
+                                   _ptr(out_scales, "out_scales", _U8), _stream(stream)), "kq_quantize_adaln")
+    return out_codes, out_scales

@@ -85,14 +85,27 @@ kq_status check_shape(int64_t tokens, int64_t d) {
 kq_status from_hip(hipError_t e) { return e == hipSuccess ? KQ_OK : KQ_ERR_HIP; }
 
 // Shared body of every quantize entry point.
+// AdaLN producer step fused in front of the transform (kq_quantize_adaln).
+struct Mod {
+  const float* stats;
+  const float* mscale;
+  const float* mshift;
+  int64_t tps;
+};
+
 kq_status run(int front, const uint16_t* X, int64_t tokens, int64_t d, const float* P, int64_t pstride,
               const uint16_t* Kbf, int variant, const float* m, float* Y, uint8_t* codes, uint8_t* scales,
-              hipStream_t stream) {
+              hipStream_t stream, const Mod* mod = nullptr) {
   kq_status st = check_shape(tokens, d);
   if (st != KQ_OK) return st;
   if (front < kq::FRONT_KRON || front > kq::FRONT_HADAMARD) return KQ_ERR_VARIANT;
   if (variant < KQ_AUTO || variant > KQ_BUTTERFLY) return KQ_ERR_VARIANT;
   if (front == kq::FRONT_KRON && pstride != 15 && pstride != 0) return KQ_ERR_SHAPE;
+  if (mod) {
+    // a tile of 32 rows never straddles two samples
+    if (mod->tps <= 0 || (mod->tps % 32 != 0 && mod->tps < tokens)) return KQ_ERR_SHAPE;
+    if (variant == KQ_BUTTERFLY || front != kq::FRONT_KRON) return KQ_ERR_VARIANT;
+  }
   if (tokens == 0) return KQ_OK;
   if (!X || !codes || !scales) return KQ_ERR_NULL;
   if (front == kq::FRONT_SMOOTH && !m) return KQ_ERR_NULL;
@@ -105,16 +118,23 @@ kq_status run(int front, const uint16_t* X, int64_t tokens, int64_t d, const flo
   if (P && !aligned(P, 4)) return KQ_ERR_ALIGN;
   if (Kbf && !aligned(Kbf, 16)) return KQ_ERR_ALIGN;
   if (m && !aligned(m, 16)) return KQ_ERR_ALIGN;
+  if (mod && ((mod->stats && !aligned(mod->stats, 8)) || (mod->mscale && !aligned(mod->mscale, 4)) ||
+              (mod->mshift && !aligned(mod->mshift, 4))))
+    return KQ_ERR_ALIGN;
 
   const int64_t nb = d / 32;
   const uint64_t n = (uint64_t)tokens * (uint64_t)d;
   const uint64_t nk = pstride == 0 ? 1 : (uint64_t)nb;
   const Range outs[] = {{codes, n / 2}, {scales, n / 32}, {Y, Y ? n * 4 : 0}};
+  const uint64_t nsamples = mod ? (uint64_t)((tokens + mod->tps - 1) / mod->tps) : 0;
   const Range ins[] = {{X, n * 2},
                        {front == kq::FRONT_KRON ? P : nullptr, nk * 60},
                        {front == kq::FRONT_KRON && variant == KQ_MFMA_DENSE ? Kbf : nullptr, nk * 3 * 2048},
-                       {front == kq::FRONT_SMOOTH ? m : nullptr, (uint64_t)d * 4}};
-  if (any_alias(outs, 3, ins, 4)) return KQ_ERR_ALIAS;
+                       {front == kq::FRONT_SMOOTH ? m : nullptr, (uint64_t)d * 4},
+                       {mod ? mod->stats : nullptr, (uint64_t)tokens * 8},
+                       {mod ? mod->mscale : nullptr, nsamples * (uint64_t)d * 4},
+                       {mod ? mod->mshift : nullptr, nsamples * (uint64_t)d * 4}};
+  if (any_alias(outs, 3, ins, 7)) return KQ_ERR_ALIAS;
 
   const int T = (int)tokens;
   if (front == kq::FRONT_KRON && variant != KQ_BUTTERFLY) {
@@ -130,7 +150,14 @@ kq_status run(int front, const uint16_t* X, int64_t tokens, int64_t d, const flo
     a.codes = codes;
     a.scales = scales;
     a.Y = Y;
-    return from_hip(kq::launch_mfma(variant == KQ_MFMA_OTF ? KSRC_PARAMS : KSRC_SPLIT, Y != nullptr, a, stream));
+    if (mod) {
+      a.stats = mod->stats;
+      a.mscale = mod->mscale;
+      a.mshift = mod->mshift;
+      a.tps = (int)(mod->tps < tokens ? mod->tps : tokens);
+    }
+    return from_hip(
+        kq::launch_mfma(variant == KQ_MFMA_OTF ? KSRC_PARAMS : KSRC_SPLIT, Y != nullptr, mod != nullptr, a, stream));
   }
   kq::QuadArgs a{};
   a.X = X;
@@ -275,6 +302,29 @@ kq_status kq_transform_f32(int front, const uint16_t* X, int64_t tokens, int64_t
   }
   return run(front, X, tokens, d, K_params, params_block_stride, K_bf16, (int)variant, ch_mult, Y, out_codes,
              out_scales, stream);
+}
+
+kq_status kq_row_stats(const uint16_t* X, int64_t tokens, int64_t d, float eps, float* row_stats,
+                       hipStream_t stream) {
+  kq_status st = check_shape(tokens, d);
+  if (st != KQ_OK) return st;
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return KQ_ERR_SHAPE;
+  if (tokens == 0) return KQ_OK;
+  if (!X || !row_stats) return KQ_ERR_NULL;
+  if (!aligned(X, 16) || !aligned(row_stats, 8)) return KQ_ERR_ALIGN;
+  const Range outs[] = {{row_stats, (uint64_t)tokens * 8}};
+  const Range ins[] = {{X, (uint64_t)tokens * (uint64_t)d * 2}};
+  if (any_alias(outs, 1, ins, 1)) return KQ_ERR_ALIAS;
+  return from_hip(kq::launch_row_stats(X, (int)tokens, (int)d, (double)eps, row_stats, stream));
+}
+
+kq_status kq_quantize_adaln(const uint16_t* X, int64_t tokens, int64_t d, const float* row_stats,
+                            const float* mod_scale, const float* mod_shift, int64_t tokens_per_sample,
+                            const float* K_params, int64_t params_block_stride, const uint16_t* K_bf16,
+                            kq_variant variant, uint8_t* out_codes, uint8_t* out_scales, hipStream_t stream) {
+  const Mod mod{row_stats, mod_scale, mod_shift, tokens_per_sample};
+  return run(kq::FRONT_KRON, X, tokens, d, K_params, params_block_stride, K_bf16, (int)variant, nullptr,
+             nullptr, out_codes, out_scales, stream, &mod);
 }
 
 }  // extern "C"

@@ -18,6 +18,7 @@ namespace kq {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 
 enum { FRONT_KRON = 0, FRONT_PLAIN = 1, FRONT_SMOOTH = 2, FRONT_HADAMARD = 3 };
 enum { LAYOUT_MFMA = 0, LAYOUT_QUAD = 1 };

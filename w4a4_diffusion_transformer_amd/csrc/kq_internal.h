@@ -26,6 +26,12 @@ struct MfmaArgs {
   uint8_t* codes;
   uint8_t* scales;
   float* Y;  // diagnostic output or nullptr
+  // AdaLN producer step (the MOD kernels): row (mean, rstd) pairs or nullptr,
+  // per-sample fp32 scale and shift [samples][d] or nullptr, rows per sample
+  const float* stats;
+  const float* mscale;
+  const float* mshift;
+  int tps;
   int ngroups, nchunks;
   int w1, r1, n2;  // second part of the grid: see above
 };
@@ -58,8 +64,9 @@ int resident_per_cu(const void* fn, int block_threads);
 // once (no second, partial round), with at least one row tile per chunk.
 int chunks_one_round(const void* fn, int block_threads, int ngroups, int ntiles);
 
-hipError_t launch_mfma(int ksrc, bool store_y, const MfmaArgs& args, hipStream_t stream);
+hipError_t launch_mfma(int ksrc, bool store_y, bool mod, const MfmaArgs& args, hipStream_t stream);
 hipError_t launch_quad(int front, bool store_y, const QuadArgs& args, hipStream_t stream);
+hipError_t launch_row_stats(const uint16_t* X, int T, int d, double eps, float* stats, hipStream_t stream);
 hipError_t launch_build(const float* P, int nb, float* K32, uint16_t* Kbf, int n_split, hipStream_t stream);
 
 }  // namespace kq

@@ -107,7 +107,30 @@ __device__ __forceinline__ void setup_a(bf16x8 A[2][3], const Params15& pv, cons
   }
 }
 
-template <int KSRC, bool STORE_Y>
+// AdaLN producer step on this lane's 8 bf16 values of one token, in fp32,
+// one IEEE operation each and in this order (no contraction): centre and
+// scale by the row statistics, times (1 + scale[c]), plus shift[c]; then
+// rounded to bf16 (nearest even).  The transform then sees exactly the bf16
+// activation an unfused LayerNorm + modulation kernel would have written.
+__device__ __forceinline__ bf16x8 modulate8(bf16x8 x, float mean, float rstd, bool norm, const float opa[8],
+                                            bool has_scale, const float sh[8], bool has_shift) {
+#pragma clang fp contract(off)
+  bf16x8 out;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float v = (float)x[i];
+    if (norm) {
+      v = v - mean;
+      v = v * rstd;
+    }
+    if (has_scale) v = v * opa[i];
+    if (has_shift) v = v + sh[i];
+    out[i] = (__bf16)v;
+  }
+  return out;
+}
+
+template <int KSRC, bool STORE_Y, bool MOD>
 __global__ __launch_bounds__(kThreads) void mfma_kernel(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_in[2][kInBytes];
   __shared__ __attribute__((aligned(16))) uint8_t lds_out[2][kOutBytes];
@@ -178,6 +201,10 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(MfmaArgs a) {
   }
 
   u32x4 pre[kAhead][kPPT];
+  // MOD: (mean, rstd) of rows 16 rt + tl of the tiles in flight, loaded with
+  // their X (a zero-range descriptor when there are no statistics).
+  u32x2 pst[kAhead][kRT];
+  u32x2 cst[kRT];
   // Wave-uniform cursors, advanced by a constant per tile: the next tile to
   // load and the next tile to write out.  `left` counts the rows from a
   // cursor to row_end (negative past it); range sizes are clamped to one
@@ -189,16 +216,29 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(MfmaArgs a) {
   int lleft = row_end - row_first;
   const uint8_t* lx = reinterpret_cast<const uint8_t*>(a.X) + (int64_t)row_first * xrow_bytes;
   const int64_t lstep = (int64_t)step_rows * xrow_bytes;
-  auto gload_next = [&](u32x4 (&r)[kPPT]) {
+  const uint8_t* lst = reinterpret_cast<const uint8_t*>(a.stats) + (int64_t)row_first * 8;
+  const int tl = lane & 15, q = lane >> 4;
+  auto gload_next = [&](int slot) {
     const auto rx = rsrc_uniform(lx, rows_in(lleft) * xrow_bytes);
 #pragma unroll
-    for (int k = 0; k < kPPT; ++k) r[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[k], 0, kNT);
+    for (int k = 0; k < kPPT; ++k) pre[slot][k] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff[k], 0, kNT);
+    if constexpr (MOD) {
+      const auto rst = rsrc_uniform(lst, a.stats ? rows_in(lleft) * 8 : 0);
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt)
+        pst[slot][rt] = __builtin_amdgcn_raw_buffer_load_b64(rst, (uint32_t)(16 * rt + tl) * 8u, 0, 0);
+      lst += (int64_t)step_rows * 8;
+    }
     lleft -= step_rows;
     lx += lstep;
   };
-  auto lwrite = [&](int buf, const u32x4 (&r)[kPPT]) {
+  auto lwrite = [&](int buf, int slot) {
 #pragma unroll
-    for (int k = 0; k < kPPT; ++k) *reinterpret_cast<u32x4*>(&lds_in[buf][lin[k]]) = r[k];
+    for (int k = 0; k < kPPT; ++k) *reinterpret_cast<u32x4*>(&lds_in[buf][lin[k]]) = pre[slot][k];
+    if constexpr (MOD) {
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) cst[rt] = pst[slot][rt];
+    }
   };
   int sleft = row_end - row_first;
   uint8_t* sc = a.codes + (int64_t)row_first * crow_bytes;
@@ -219,17 +259,38 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(MfmaArgs a) {
     ss += sstep;
   };
 
-  const int tl = lane & 15, q = lane >> 4;
-  int crow = row_first;  // first row of the tile being computed (diagnostic store only)
+  int crow = row_first;  // first row of the tile being computed
+  // MOD: this lane's (1 + scale, shift) for its 8 channels, of sample cur_s
+  float opa[8], sh[8];
+  int cur_s = -1;
   auto compute = [&](int buf) {
     if (!mine) return;  // wave-uniform
     const int jl = wv, j = jg + jl;
+    if constexpr (MOD) {
+      // tiles never straddle samples (tokens_per_sample is a multiple of the tile rows, or covers all rows)
+      const int smp = crow / a.tps;
+      if (smp != cur_s) {  // wave-uniform; a few times per workgroup at most
+        cur_s = smp;
+        const int64_t off = (int64_t)smp * a.d + 32 * j + 8 * q;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          opa[i] = a.mscale ? 1.0f + a.mscale[off + i] : 1.0f;
+          sh[i] = a.mshift ? a.mshift[off + i] : 0.0f;
+        }
+      }
+    }
     // all MFMAs of the tile first, so their latency overlaps the epilogues
     float y[kRT][8];
 #pragma unroll
     for (int rt = 0; rt < kRT; ++rt) {
       const int tr = 16 * rt + tl;
-      const bf16x8 xb = *reinterpret_cast<const bf16x8*>(&lds_in[buf][tr * kInStride + 64 * jl + 16 * q]);
+      bf16x8 xb = *reinterpret_cast<const bf16x8*>(&lds_in[buf][tr * kInStride + 64 * jl + 16 * q]);
+      if constexpr (MOD) {
+        xb = modulate8(xb, __uint_as_float(cst[rt][0]), __uint_as_float(cst[rt][1]), a.stats != nullptr, opa,
+                       a.mscale != nullptr, sh, a.mshift != nullptr);
+        // the exact path reads the block back from this tile
+        *reinterpret_cast<bf16x8*>(&lds_in[buf][tr * kInStride + 64 * jl + 16 * q]) = xb;
+      }
       f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
       acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[0][2], xb, acc0, 0, 0, 0);
       acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[1][2], xb, acc1, 0, 0, 0);
@@ -283,10 +344,10 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(MfmaArgs a) {
   // The first tile's loads go out before the K setup, which overlaps them;
   // the loads of the next tiles follow the setup, so that at the start of the
   // kernel (every workgroup issuing at once) the first tiles arrive early.
-  gload_next(pre[0]);
+  gload_next(0);
   if (mine) setup_a<KSRC>(A, pv, KSRC == KSRC_SPLIT ? a.Kbf + (int64_t)(jg + wv) * a.kstride : nullptr, lane, lds_g[wv]);
 #pragma unroll
-  for (int k = 1; k < kAhead; ++k) gload_next(pre[k]);
+  for (int k = 1; k < kAhead; ++k) gload_next(k);
 
   // Per tile s: stage tile s into LDS, fetch tile s + kAhead, barrier, write
   // out tile s - 1, compute tile s.  Every memory instruction is issued
@@ -294,8 +355,8 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(MfmaArgs a) {
   // kAhead tiles stay in flight across the barrier.  Tile 0 is peeled: it has
   // no predecessor to write out.
   if (nsteps == 0) return;  // workgroup-uniform
-  lwrite(0, pre[0]);
-  gload_next(pre[0]);
+  lwrite(0, 0);
+  gload_next(0);
   __syncthreads();
   compute(0);
   crow += step_rows;
@@ -305,8 +366,8 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(MfmaArgs a) {
       const int s = it + k;
       if (s < nsteps) {
         const int buf = s & 1;
-        lwrite(buf, pre[(1 + k) % kAhead]);
-        gload_next(pre[(1 + k) % kAhead]);
+        lwrite(buf, (1 + k) % kAhead);
+        gload_next((1 + k) % kAhead);
         __syncthreads();
         gstore_next(buf ^ 1);
         compute(buf);
@@ -320,12 +381,19 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(MfmaArgs a) {
 
 }  // namespace
 
-hipError_t launch_mfma(int ksrc, bool store_y, const MfmaArgs& args, hipStream_t stream) {
+hipError_t launch_mfma(int ksrc, bool store_y, bool mod, const MfmaArgs& args, hipStream_t stream) {
   const void* fn;
-  if (ksrc == KSRC_PARAMS)
-    fn = store_y ? (const void*)&mfma_kernel<KSRC_PARAMS, true> : (const void*)&mfma_kernel<KSRC_PARAMS, false>;
-  else
-    fn = store_y ? (const void*)&mfma_kernel<KSRC_SPLIT, true> : (const void*)&mfma_kernel<KSRC_SPLIT, false>;
+  if (mod) {
+    if (store_y) return hipErrorInvalidValue;
+    fn = ksrc == KSRC_PARAMS ? (const void*)&mfma_kernel<KSRC_PARAMS, false, true>
+                             : (const void*)&mfma_kernel<KSRC_SPLIT, false, true>;
+  } else if (ksrc == KSRC_PARAMS) {
+    fn = store_y ? (const void*)&mfma_kernel<KSRC_PARAMS, true, false>
+                 : (const void*)&mfma_kernel<KSRC_PARAMS, false, false>;
+  } else {
+    fn = store_y ? (const void*)&mfma_kernel<KSRC_SPLIT, true, false>
+                 : (const void*)&mfma_kernel<KSRC_SPLIT, false, false>;
+  }
   MfmaArgs a = args;
   const int nt = (a.T + kRows - 1) / kRows;
   a.ngroups = (a.nb + kCB - 1) / kCB;
