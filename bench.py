@@ -121,6 +121,87 @@ def shape_table(kq, torch, np, synth, dev):
     return out
 
 
+def adaln_table(kq, torch, np, synth, dev):
+    """The fused AdaLN producer step + quantizer against the unfused pipeline.
+
+    Unfused: a LayerNorm + modulation written as torch ops (fp32 math, one bf16
+    tensor written back to HBM) followed by kq_quantize on that tensor.  Fused:
+    kq_quantize_adaln on the raw activation with the row statistics.  The row
+    statistics kernel is timed on its own.  Inputs: FLUX.1-schnell width
+    (one sample of 4608 tokens x 3072) and PixArt-Sigma width (2 x 4096 tokens
+    x 1152), N(0,1) activations with 1% outlier channels, AdaLN vectors with 1%
+    amplified channels."""
+    out = {}
+    for name, T, d, tps in (("flux_x1", 4608, 3072, 4608), ("pixart_x1", 8192, 1152, 4096)):
+        X = synth.random_matrix(T, d, seed=41, n_outliers=d // 100, mult=50.0, token_sigma=0.5)
+        P = synth.random_params(d // 32, seed=42)
+        ns = (T + tps - 1) // tps
+        sc, sh = synth.adaln_vectors(ns, d, seed=43)
+        nbytes = BYTES_PER_ELEM * T * d
+        copies = max(2, int(np.ceil(512e6 / nbytes)))
+        X0 = torch.from_numpy(X.view(np.int16)).to(dev)
+        Xs = [X0] + [X0.clone() for _ in range(copies - 1)]
+        outs = [kq.alloc_outputs(X0) for _ in range(copies)]
+        Pd = torch.from_numpy(P).to(dev)
+        scd = torch.from_numpy(sc).to(dev)
+        shd = torch.from_numpy(sh).to(dev)
+        sts = [torch.empty((T, 2), dtype=torch.float32, device=dev) for _ in range(copies)]
+        for i in range(copies):
+            kq.kq_row_stats(Xs[i], 1e-6, sts[i])
+        L = kq.lib()
+        stream = torch.cuda.current_stream().cuda_stream
+        xs = [x.data_ptr() for x in Xs]
+        ops = [(c_.data_ptr(), s_.data_ptr()) for c_, s_ in outs]
+        stp = [s_.data_ptr() for s_ in sts]
+        rep_sc = scd.repeat_interleave(tps, 0)[:T]
+        rep_sh = shd.repeat_interleave(tps, 0)[:T]
+
+        def fused(i):
+            return L.kq_quantize_adaln(xs[i], T, d, stp[i], scd.data_ptr(), shd.data_ptr(), tps, Pd.data_ptr(), 15,
+                                       None, kq.KQ_AUTO, *ops[i], stream)
+
+        def stats(i):
+            return L.kq_row_stats(xs[i], T, d, 1e-6, stp[i], stream)
+
+        def unfused(i):
+            st = sts[i]
+            xm = ((Xs[i].view(torch.bfloat16).float() - st[:, :1]) * st[:, 1:] * (1.0 + rep_sc) + rep_sh).to(torch.bfloat16)
+            return L.kq_quantize_ex(xm.data_ptr(), T, d, Pd.data_ptr(), 15, None, kq.KQ_AUTO, *ops[i], stream)
+
+        row = {"T": T, "d": d, "tokens_per_sample": tps}
+        for label, fn in (("fused_quantize_adaln", fused), ("row_stats", stats), ("unfused_torch_eager_modulate_then_quantize", unfused)):
+            reps = max(60, 4 * copies)
+            t_warm = time.perf_counter() + 0.1
+            while time.perf_counter() < t_warm:
+                for i in range(reps):
+                    assert fn(i % copies) == 0
+                torch.cuda.synchronize()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(reps):
+                fn(i % copies)
+            b.record()
+            torch.cuda.synchronize()
+            sec = a.elapsed_time(b) * 1e-3 / reps
+            row[label] = {"us": round(sec * 1e6, 2)}
+            if label == "fused_quantize_adaln":
+                fb = nbytes + 8 * T
+                row[label].update({"GBps": round(fb / sec / 1e9, 1), "pct_peak": round(100 * fb / sec / 1e9 / HBM_PEAK_GBS, 1)})
+            if label == "row_stats":
+                rb = 2 * T * d + 8 * T
+                row[label].update({"GBps": round(rb / sec / 1e9, 1)})
+        row["unfused_over_fused_time"] = round(row["unfused_torch_eager_modulate_then_quantize"]["us"] / row["fused_quantize_adaln"]["us"], 3)
+        # HBM bytes: fused = X read once + codes/scales + stats; an unfused pipeline with one ideal
+        # producer kernel moves X in, X_mod out, then the quantizer's X_mod in + codes/scales
+        row["algorithmic_bytes_fused"] = int(nbytes + 8 * T)
+        row["algorithmic_bytes_unfused_min"] = int(nbytes + 4 * T * d + 8 * T)
+        out[name] = row
+        del Xs, outs
+        print(f"# adaln {name}: " + json.dumps(row), file=sys.stderr, flush=True)
+    return out
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +211,7 @@ def parse():
     ap.add_argument("--no-compare", action="store_true", help="skip the comparison kernels")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-shapes", action="store_true", help="skip the per-shape table of the other workloads")
+    ap.add_argument("--no-adaln", action="store_true", help="skip the fused AdaLN producer-step table")
     ap.add_argument("--profile-pass", action="store_true",
                     help="few launches of each kernel plus a plain copy of known size, for rocprofv3 counter runs")
     return ap.parse_args()
@@ -250,6 +332,9 @@ def main():
     per_shape = None
     if not args.no_shapes:
         per_shape = shape_table(kq, torch, np, synth, dev)
+    adaln = None
+    if not args.no_adaln:
+        adaln = adaln_table(kq, torch, np, synth, dev)
 
     variant_name = args.variant
     kernel = kq.variant_name(kq.kq_auto_variant(T, d, True, False)) if variant_name == "auto" else variant_name
@@ -281,6 +366,7 @@ def main():
         "cpu_baseline": cpu,
         "comparison": comparison,
         "per_shape": per_shape,
+        "adaln_fused": adaln,
     }
     print(json.dumps(out), flush=True)
 
