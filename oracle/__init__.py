@@ -61,6 +61,8 @@ def lib():
         L.kqo_fwht32.argtypes = [vp]
         L.kqo_det.argtypes = [vp, ci]
         L.kqo_det.restype = d
+        L.kqo_build_blocks_inverse_t.argtypes = [vp, i64, i64, vp, vp, ci]
+        L.kqo_dequant_rows.argtypes = [vp, vp, i64, i64, vp]
         L.kqo_row_stats.argtypes = [vp, i64, i64, d, vp]
         L.kqo_row_stats.restype = ci
         L.kqo_adaln_rows.argtypes = [vp, i64, i64, vp, vp, vp, i64, vp]
@@ -205,6 +207,31 @@ def quantize_rows(front: int, X: np.ndarray, P=None, pstride: int = 15, m=None, 
     if want_y:
         out["y32"], out["yhat"] = y32, yhat
     return out
+
+
+def build_blocks_inverse_t(P, nb: int, pstride: int = 15, n_split: int = 3):
+    """Blocks of the weight fold: (K^-T as fp32 [nb,32,32] (r, c), its bf16 split [nb,n_split,32,32] (c, r))."""
+    P = np.ascontiguousarray(P, dtype=np.float32).reshape(-1)
+    K32 = np.empty((nb, 32, 32), dtype=np.float32)
+    Kbf = np.empty((nb, n_split, 32, 32), dtype=np.uint16)
+    lib().kqo_build_blocks_inverse_t(P.ctypes.data, nb, pstride, K32.ctypes.data, Kbf.ctypes.data, n_split)
+    return K32, Kbf
+
+
+def dequant_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """MXFP4 codes [n, d/2] + scales [n, d/32] -> fp64 values [n, d]."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    n, d = codes.shape[0], codes.shape[1] * 2
+    out = np.empty((n, d), dtype=np.float64)
+    lib().kqo_dequant_rows(codes.ctypes.data, scales.ctypes.data, n, d, out.ctypes.data)
+    return out
+
+
+def gemm_mx(a_codes, a_scales, b_codes, b_scales) -> np.ndarray:
+    """Y = deq(A) deq(B)^T in fp64 (A [M, K] and B [N, K] as MXFP4 codes and scales).
+    The dequantized products are exact in fp64; the sum is a BLAS fp64 matmul."""
+    return dequant_rows(a_codes, a_scales) @ dequant_rows(b_codes, b_scales).T
 
 
 def row_stats(X: np.ndarray, eps: float = 1e-6) -> np.ndarray:

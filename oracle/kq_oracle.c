@@ -347,3 +347,41 @@ int kqo_adaln_rows(const uint16_t* X, int64_t T, int64_t d, const float* stats, 
   }
   return 0;
 }
+
+/* The bf16 split of one fp32 block into n_split terms, stored transposed ([s][c][r]). */
+static void split_block(const float k32[1024], uint16_t* Kbf_block, int n_split) {
+  for (int r = 0; r < 32; ++r)
+    for (int c = 0; c < 32; ++c) {
+      float rest = k32[r * 32 + c];
+      for (int s = 0; s < n_split; ++s) {
+        const uint16_t h = f32_to_bf16_rne(rest);
+        Kbf_block[(s * 32 + c) * 32 + r] = h;
+        rest = rest - bf16_to_f32(h);
+      }
+    }
+}
+
+void kqo_build_blocks_inverse_t(const float* P, int64_t nb, int64_t pstride, float* K32, uint16_t* Kbf,
+                                int n_split) {
+  for (int64_t j = 0; j < nb; ++j) {
+    double Kinv[1024];
+    kqo_kron_inverse(P + j * pstride, Kinv);
+    float k32[1024];
+    for (int r = 0; r < 32; ++r)
+      for (int c = 0; c < 32; ++c) k32[r * 32 + c] = (float)Kinv[c * 32 + r];  /* transpose */
+    if (K32) memcpy(K32 + j * 1024, k32, sizeof k32);
+    if (Kbf) split_block(k32, Kbf + j * (int64_t)n_split * 1024, n_split);
+  }
+}
+
+/* E2M1 magnitudes by index and the E8M0 scale (OCP MX v1.0). */
+void kqo_dequant_rows(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t d, double* out) {
+  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  for (int64_t t = 0; t < n; ++t)
+    for (int64_t c = 0; c < d; ++c) {
+      const uint8_t byte = codes[t * (d / 2) + c / 2];
+      const int code = (c & 1) ? (byte >> 4) : (byte & 15);
+      const double v = mag[code & 7] * ldexp(1.0, (int)scales[t * (d / 32) + c / 32] - 127);
+      out[t * d + c] = (code & 8) ? -v : v;
+    }
+}

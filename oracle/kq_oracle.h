@@ -47,6 +47,21 @@ void kqo_block_f32(const float P[15], float K32[1024]);
  */
 void kqo_build_blocks(const float* P, int64_t nb, int64_t pstride, float* K32, uint16_t* Kbf, int n_split);
 
+/*
+ * Blocks for the offline weight fold (Pith review, circularity check:
+ * Eq. (1), A T (W T^-T)^T = A W^T).  For the linear layer y = x W^T each row
+ * of W is multiplied on the right by K(j)^-T, block by block, where
+ * K^-T = (G1^-1)^T (x) ... (x) (G5^-1)^T.  Entry [r][c] of block j is the
+ * product, in fp64 and factor order, of G_k^-1[bit(c)][bit(r)] over the five
+ * factors, rounded once to fp32 (K32 [nb][32 r][32 c]); the bf16 split Kbf as
+ * in kqo_build_blocks.  Either output may be NULL.
+ */
+void kqo_build_blocks_inverse_t(const float* P, int64_t nb, int64_t pstride, float* K32, uint16_t* Kbf,
+                                int n_split);
+
+/* MXFP4 dequantization: out[t][c] = E2M1(code) * 2^(scale - 127) in fp64 ([n][d]). */
+void kqo_dequant_rows(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t d, double* out);
+
 /* E2M1 magnitude index (0..7) of |v| under round-to-nearest-even with saturation. */
 int kqo_e2m1_index(double m);
 /* E8M0 scale byte for a block amax: floor(log2 amax) - 2 + 127 clamped to [0, 254]; amax == 0 -> 0. */
