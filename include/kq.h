@@ -104,7 +104,7 @@ typedef enum {
 typedef enum { KQ_FRONT_KRON = 0, KQ_FRONT_PLAIN = 1, KQ_FRONT_SMOOTH = 2, KQ_FRONT_HADAMARD = 3 } kq_front;
 
 /* ABI version of this header (bumped on any signature or layout change). */
-#define KQ_ABI_VERSION 2
+#define KQ_ABI_VERSION 3
 int kq_abi_version(void);
 
 /* Static, never-NULL description of a status code. */
@@ -224,6 +224,35 @@ kq_status kq_quantize_adaln(const uint16_t* X, int64_t tokens, int64_t d, const 
                             const float* mod_scale, const float* mod_shift, int64_t tokens_per_sample,
                             const float* K_params, int64_t params_block_stride, const uint16_t* K_bf16,
                             kq_variant variant, uint8_t* out_codes, uint8_t* out_scales, hipStream_t stream);
+
+/*
+ * Blocks of the offline weight fold (Pith review, circularity check:
+ * Eq. (1), A T (W T^-T)^T = A W^T): as kq_build_blocks, for
+ * K^-T = (G1^-1)^T (x) ... (x) (G5^-1)^T with G^-1 = [[l b + 1/a, -b],
+ * [-l a, a]] (each entry the fp64 product in factor order, rounded once to
+ * fp32; same layouts and errors).  The folded, quantized weight is then
+ * kq_quantize_ex(W, N_out, K_in, NULL, 15, K_bf16 of these blocks,
+ * KQ_MFMA_DENSE, w_codes, w_scales, stream) for a bf16 weight W [N_out][K_in]
+ * (rows = output features), i.e. every weight row times T^-T, quantized to
+ * MXFP4 along K_in.
+ */
+kq_status kq_build_blocks_inverse_t(const float* K_params, int64_t nb, float* K_f32, uint16_t* K_bf16, int n_split,
+                                    hipStream_t stream);
+
+/*
+ * W4A4 GEMM on the scaled FP4 matrix cores: Y[m][n] = sum_k a[m][k] b[n][k]
+ * with a = E2M1(code) * 2^(scale - 127) from A (codes [M][K/2], scales
+ * [M][K/32], the layout kq_quantize writes) and b likewise from B [N][K]
+ * (a folded weight from kq_build_blocks_inverse_t + kq_quantize_ex).  Each
+ * product is exact; sums are fp32 (per element error below K 2^-24 sum|a b|
+ * in practice).  Writes Y_f32 [M][N] fp32 and/or Y_bf16 [M][N] bf16 (nearest
+ * even), either may be NULL but not both.  K a positive multiple of 32
+ * (<= 2^24), M <= 2^23, N <= 2^22, else KQ_ERR_SHAPE; codes 16-byte aligned;
+ * outputs must not overlap inputs.  M == 0 or N == 0 returns KQ_OK.
+ */
+kq_status kq_gemm_mx(const uint8_t* A_codes, const uint8_t* A_scales, int64_t M, const uint8_t* B_codes,
+                     const uint8_t* B_scales, int64_t N, int64_t K, float* Y_f32, uint16_t* Y_bf16,
+                     hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -63,6 +63,8 @@ def lib():
         L.kqo_det.restype = d
         L.kqo_build_blocks_inverse_t.argtypes = [vp, i64, i64, vp, vp, ci]
         L.kqo_dequant_rows.argtypes = [vp, vp, i64, i64, vp]
+        L.kqo_quantize_rows_blocks.argtypes = [vp, i64, i64, vp, i64, i64, i64, vp, vp, vp, vp]
+        L.kqo_quantize_rows_blocks.restype = ci
         L.kqo_row_stats.argtypes = [vp, i64, i64, d, vp]
         L.kqo_row_stats.restype = ci
         L.kqo_adaln_rows.argtypes = [vp, i64, i64, vp, vp, vp, i64, vp]
@@ -216,6 +218,41 @@ def build_blocks_inverse_t(P, nb: int, pstride: int = 15, n_split: int = 3):
     Kbf = np.empty((nb, n_split, 32, 32), dtype=np.uint16)
     lib().kqo_build_blocks_inverse_t(P.ctypes.data, nb, pstride, K32.ctypes.data, Kbf.ctypes.data, n_split)
     return K32, Kbf
+
+
+def quantize_rows_blocks(X: np.ndarray, K32: np.ndarray, want_y: bool = False, threads: int = 1):
+    """KroQuant front-end + MXFP4 with given fp32 blocks K32 [nb, 32, 32] (r, c) (e.g. the weight
+    fold's K^-T).  Returns dict(codes, scales[, y32, yhat]) like quantize_rows."""
+    X = np.ascontiguousarray(X, dtype=np.uint16)
+    K32 = np.ascontiguousarray(K32, dtype=np.float32)
+    T, d = X.shape
+    kstride = 0 if K32.shape[0] == 1 and d > 32 else 1024
+    codes = np.zeros((T, d // 2), dtype=np.uint8)
+    scales = np.zeros((T, d // 32), dtype=np.uint8)
+    y32 = np.zeros((T, d), dtype=np.float32) if want_y else None
+    yhat = np.zeros((T, d), dtype=np.float64) if want_y else None
+    L = lib()
+
+    def run(a: int, b: int) -> int:
+        if a >= b:
+            return 0
+        return L.kqo_quantize_rows_blocks(X.ctypes.data, T, d, K32.ctypes.data, kstride, a, b,
+                                          codes[a:].ctypes.data, scales[a:].ctypes.data,
+                                          None if y32 is None else y32[a:].ctypes.data,
+                                          None if yhat is None else yhat[a:].ctypes.data)
+
+    if threads <= 1 or T < 2 * threads:
+        rcs = [run(0, T)]
+    else:
+        step = (T + threads - 1) // threads
+        with ThreadPoolExecutor(threads) as ex:
+            rcs = list(ex.map(lambda i: run(i * step, min(T, (i + 1) * step)), range(threads)))
+    if any(rcs):
+        raise ValueError("oracle rejected its arguments")
+    out = {"codes": codes, "scales": scales}
+    if want_y:
+        out["y32"], out["yhat"] = y32, yhat
+    return out
 
 
 def dequant_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:

@@ -385,3 +385,37 @@ void kqo_dequant_rows(const uint8_t* codes, const uint8_t* scales, int64_t n, in
       out[t * d + c] = (code & 8) ? -v : v;
     }
 }
+
+/*
+ * The KroQuant front-end with the fp32 blocks given instead of their 15
+ * scalars (K32 [nb][32 r][32 c], block j at K32 + j * kstride, kstride 1024
+ * or 0): y = RNE_fp32(sum_r x[r] K[r][c]) with the fp64 sum of exact
+ * products, then MXFP4, exactly as kqo_quantize_rows does for KQO_KRON.  Used
+ * for the weight fold with the blocks of kqo_build_blocks_inverse_t.
+ */
+int kqo_quantize_rows_blocks(const uint16_t* X, int64_t T, int64_t d, const float* K32, int64_t kstride,
+                             int64_t row0, int64_t row1, uint8_t* codes, uint8_t* scales, float* y32, double* yhat) {
+  if (!X || !K32 || d <= 0 || d % 32 != 0 || T < 0 || row0 < 0 || row1 > T || row0 > row1 || !codes || !scales ||
+      (kstride != 0 && kstride != 1024))
+    return 1;
+  const int64_t nb = d / 32;
+  for (int64_t t = row0; t < row1; ++t) {
+    const int64_t ro = t - row0;
+    for (int64_t j = 0; j < nb; ++j) {
+      double x[32], yh[32];
+      float y[32];
+      for (int r = 0; r < 32; ++r) x[r] = bf16_to_f64(X[t * d + 32 * j + r]);
+      const float* K = K32 + j * kstride;
+      for (int cc = 0; cc < 32; ++cc) {
+        double s = 0.0;
+        for (int r = 0; r < 32; ++r) s = s + x[r] * (double)K[r * 32 + cc];
+        yh[cc] = s;
+        y[cc] = (float)s;
+      }
+      kqo_quantize_block(y, codes + ro * (d / 2) + 16 * j, scales + ro * nb + j);
+      if (y32) memcpy(y32 + ro * d + 32 * j, y, sizeof y);
+      if (yhat) memcpy(yhat + ro * d + 32 * j, yh, sizeof yh);
+    }
+  }
+  return 0;
+}

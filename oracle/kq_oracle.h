@@ -59,6 +59,14 @@ void kqo_build_blocks(const float* P, int64_t nb, int64_t pstride, float* K32, u
 void kqo_build_blocks_inverse_t(const float* P, int64_t nb, int64_t pstride, float* K32, uint16_t* Kbf,
                                 int n_split);
 
+/*
+ * The KroQuant front-end with given fp32 blocks (K32 [nb][32 r][32 c], block j
+ * at K32 + j * kstride, kstride 1024 or 0) in place of the 15 scalars; same
+ * arithmetic and outputs as kqo_quantize_rows with KQO_KRON.  Returns 0 or 1.
+ */
+int kqo_quantize_rows_blocks(const uint16_t* X, int64_t T, int64_t d, const float* K32, int64_t kstride,
+                             int64_t row0, int64_t row1, uint8_t* codes, uint8_t* scales, float* y32, double* yhat);
+
 /* MXFP4 dequantization: out[t][c] = E2M1(code) * 2^(scale - 127) in fp64 ([n][d]). */
 void kqo_dequant_rows(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t d, double* out);
 

@@ -118,3 +118,14 @@ def test_eq1_with_quantization_kroquant_beats_plain_on_outliers():
     err = lambda y: np.linalg.norm(y - exact) / np.linalg.norm(exact)
     # measured on this workload: 0.168 against 0.188 (relative Frobenius error of Y)
     assert err(y_kq) < 0.95 * err(y_plain), (err(y_kq), err(y_plain))
+
+
+def test_quantize_with_given_blocks_equals_kron_front_end():
+    """Given the fp32 blocks of K itself, the dense-block path reproduces the 15-scalar path bit for bit."""
+    X = synth.random_matrix(40, 320, seed=34, n_outliers=3, mult=40.0)
+    P = synth.random_params(10, seed=35, sigma_lb=0.3, sigma_a=0.3)
+    K32, _ = oracle.build_blocks(P, 10)
+    a = oracle.quantize_rows_blocks(X, K32, want_y=True)
+    b = oracle.quantize_rows(oracle.KRON, X, P, want_y=True)
+    for k in ("codes", "scales", "y32", "yhat"):
+        np.testing.assert_array_equal(a[k], b[k])

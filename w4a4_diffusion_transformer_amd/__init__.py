@@ -20,6 +20,7 @@ __all__ = [
     "lib", "kq_abi_version", "kq_status_str", "kq_build_blocks", "kq_quantize", "kq_quantize_ex",
     "kq_mx_quantize", "kq_smooth_quantize", "kq_hadamard_quantize", "kq_transform_f32",
     "alloc_outputs", "LIB_PATH", "kq_auto_variant", "variant_name", "kq_row_stats", "kq_quantize_adaln",
+    "kq_build_blocks_inverse_t", "kq_gemm_mx",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkq.so")
@@ -59,9 +60,12 @@ def lib() -> ctypes.CDLL:
         L.kq_auto_variant.argtypes = [i64, i64, ci, ci]
         L.kq_auto_variant.restype = ci
         L.kq_row_stats.argtypes = [vp, i64, i64, ctypes.c_float, vp, vp]
+        L.kq_build_blocks_inverse_t.argtypes = [vp, i64, vp, vp, ci, vp]
+        L.kq_gemm_mx.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, vp, vp]
         L.kq_quantize_adaln.argtypes = [vp, i64, i64, vp, vp, vp, i64, vp, i64, vp, ci, vp, vp, vp]
         for name in ("kq_build_blocks", "kq_quantize", "kq_quantize_ex", "kq_mx_quantize", "kq_smooth_quantize",
-                     "kq_hadamard_quantize", "kq_transform_f32", "kq_row_stats", "kq_quantize_adaln"):
+                     "kq_hadamard_quantize", "kq_transform_f32", "kq_row_stats", "kq_quantize_adaln",
+                     "kq_build_blocks_inverse_t", "kq_gemm_mx"):
             getattr(L, name).restype = ci
         _lib = L
     return _lib
@@ -207,3 +211,24 @@ def kq_quantize_adaln(X, row_stats, mod_scale, mod_shift, tokens_per_sample: int
                                    _ptr(K_bf16, "K_bf16", _BF16), int(variant), _ptr(out_codes, "out_codes", _U8),
                                    _ptr(out_scales, "out_scales", _U8), _stream(stream)), "kq_quantize_adaln")
     return out_codes, out_scales
+
+
+def kq_build_blocks_inverse_t(K_params, nb: int, K_f32=None, K_bf16=None, n_split: int = 3, stream=None):
+    """Blocks K^-T of the weight fold (fp32 [nb,32,32] and/or transposed bf16 split [nb,n_split,32,32])."""
+    _check(lib().kq_build_blocks_inverse_t(_ptr(K_params, "K_params", _F32), nb, _ptr(K_f32, "K_f32", _F32),
+                                           _ptr(K_bf16, "K_bf16", _BF16), n_split, _stream(stream)),
+           "kq_build_blocks_inverse_t")
+    return K_f32, K_bf16
+
+
+def kq_gemm_mx(a_codes, a_scales, b_codes, b_scales, y_f32=None, y_bf16=None, stream=None):
+    """Y = deq(A) deq(B)^T: A codes [M, K/2] + scales [M, K/32], B codes [N, K/2] + scales [N, K/32]."""
+    M, N = a_codes.shape[0], b_codes.shape[0]
+    K = a_codes.shape[1] * 2
+    if b_codes.shape[1] * 2 != K:
+        raise ValueError("A and B must have the same K")
+    _check(lib().kq_gemm_mx(_ptr(a_codes, "a_codes", _U8), _ptr(a_scales, "a_scales", _U8), M,
+                            _ptr(b_codes, "b_codes", _U8), _ptr(b_scales, "b_scales", _U8), N, K,
+                            _ptr(y_f32, "y_f32", _F32), _ptr(y_bf16, "y_bf16", _BF16), _stream(stream)),
+           "kq_gemm_mx")
+    return y_f32, y_bf16

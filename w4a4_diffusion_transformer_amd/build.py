@@ -26,7 +26,7 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
 
-SOURCES = ["kq_api.hip", "kq_mfma.hip", "kq_quad.hip", "kq_build.hip", "kq_stats.hip"]
+SOURCES = ["kq_api.hip", "kq_mfma.hip", "kq_quad.hip", "kq_build.hip", "kq_stats.hip", "kq_gemm.hip"]
 
 
 def _compile(src: str) -> str:

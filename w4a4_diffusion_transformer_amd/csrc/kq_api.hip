@@ -173,6 +173,20 @@ kq_status run(int front, const uint16_t* X, int64_t tokens, int64_t d, const flo
   return from_hip(kq::launch_quad(front, Y != nullptr, a, stream));
 }
 
+kq_status build_blocks(const float* K_params, int64_t nb, float* K_f32, uint16_t* K_bf16, int n_split,
+                       int inverse_t, hipStream_t stream) {
+  if (nb <= 0 || nb >= (int64_t(1) << 20)) return KQ_ERR_SHAPE;
+  if (K_bf16 && (n_split < 1 || n_split > 3)) return KQ_ERR_SHAPE;
+  if (!K_params || (!K_f32 && !K_bf16)) return KQ_ERR_NULL;
+  if (!aligned(K_params, 4) || (K_f32 && !aligned(K_f32, 4)) || (K_bf16 && !aligned(K_bf16, 16)))
+    return KQ_ERR_ALIGN;
+  const uint64_t n = (uint64_t)nb;
+  const Range outs[] = {{K_f32, n * 4096}, {K_bf16, K_bf16 ? n * 2048 * (uint64_t)n_split : 0}};
+  const Range ins[] = {{K_params, n * 60}};
+  if (any_alias(outs, 2, ins, 1)) return KQ_ERR_ALIAS;
+  return from_hip(kq::launch_build(K_params, (int)nb, K_f32, K_bf16, K_bf16 ? n_split : 0, inverse_t, stream));
+}
+
 }  // namespace
 
 namespace kq {
@@ -244,16 +258,12 @@ const char* kq_status_str(kq_status s) {
 
 kq_status kq_build_blocks(const float* K_params, int64_t nb, float* K_f32, uint16_t* K_bf16, int n_split,
                           hipStream_t stream) {
-  if (nb <= 0 || nb >= (int64_t(1) << 20)) return KQ_ERR_SHAPE;
-  if (K_bf16 && (n_split < 1 || n_split > 3)) return KQ_ERR_SHAPE;
-  if (!K_params || (!K_f32 && !K_bf16)) return KQ_ERR_NULL;
-  if (!aligned(K_params, 4) || (K_f32 && !aligned(K_f32, 4)) || (K_bf16 && !aligned(K_bf16, 16)))
-    return KQ_ERR_ALIGN;
-  const uint64_t n = (uint64_t)nb;
-  const Range outs[] = {{K_f32, n * 4096}, {K_bf16, K_bf16 ? n * 2048 * (uint64_t)n_split : 0}};
-  const Range ins[] = {{K_params, n * 60}};
-  if (any_alias(outs, 2, ins, 1)) return KQ_ERR_ALIAS;
-  return from_hip(kq::launch_build(K_params, (int)nb, K_f32, K_bf16, K_bf16 ? n_split : 0, stream));
+  return build_blocks(K_params, nb, K_f32, K_bf16, n_split, 0, stream);
+}
+
+kq_status kq_build_blocks_inverse_t(const float* K_params, int64_t nb, float* K_f32, uint16_t* K_bf16, int n_split,
+                                    hipStream_t stream) {
+  return build_blocks(K_params, nb, K_f32, K_bf16, n_split, 1, stream);
 }
 
 kq_variant kq_auto_variant(int64_t tokens, int64_t d, int has_params, int has_split) {
@@ -325,6 +335,24 @@ kq_status kq_quantize_adaln(const uint16_t* X, int64_t tokens, int64_t d, const 
   const Mod mod{row_stats, mod_scale, mod_shift, tokens_per_sample};
   return run(kq::FRONT_KRON, X, tokens, d, K_params, params_block_stride, K_bf16, (int)variant, nullptr,
              nullptr, out_codes, out_scales, stream, &mod);
+}
+
+kq_status kq_gemm_mx(const uint8_t* A_codes, const uint8_t* A_scales, int64_t M, const uint8_t* B_codes,
+                     const uint8_t* B_scales, int64_t N, int64_t K, float* Y_f32, uint16_t* Y_bf16,
+                     hipStream_t stream) {
+  if (M < 0 || N < 0 || K <= 0 || K % 32 != 0) return KQ_ERR_SHAPE;
+  if (M > (int64_t(1) << 23) || N > (int64_t(1) << 22) || K > (int64_t(1) << 24)) return KQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return KQ_OK;
+  if (!A_codes || !A_scales || !B_codes || !B_scales || (!Y_f32 && !Y_bf16)) return KQ_ERR_NULL;
+  if (!aligned(A_codes, 16) || !aligned(B_codes, 16) || (Y_f32 && !aligned(Y_f32, 4)) ||
+      (Y_bf16 && !aligned(Y_bf16, 2)))
+    return KQ_ERR_ALIGN;
+  const uint64_t mk = (uint64_t)M * (uint64_t)K, nk = (uint64_t)N * (uint64_t)K, mn = (uint64_t)M * (uint64_t)N;
+  const Range outs[] = {{Y_f32, Y_f32 ? mn * 4 : 0}, {Y_bf16, Y_bf16 ? mn * 2 : 0}};
+  const Range ins[] = {{A_codes, mk / 2}, {A_scales, mk / 32}, {B_codes, nk / 2}, {B_scales, nk / 32}};
+  if (any_alias(outs, 2, ins, 4)) return KQ_ERR_ALIAS;
+  kq::GemmArgs g{A_codes, A_scales, B_codes, B_scales, (int)M, (int)N, (int)K, Y_f32, Y_bf16};
+  return from_hip(kq::launch_gemm(g, stream));
 }
 
 }  // extern "C"

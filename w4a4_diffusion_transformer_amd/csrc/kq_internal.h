@@ -66,7 +66,21 @@ int chunks_one_round(const void* fn, int block_threads, int ngroups, int ntiles)
 
 hipError_t launch_mfma(int ksrc, bool store_y, bool mod, const MfmaArgs& args, hipStream_t stream);
 hipError_t launch_quad(int front, bool store_y, const QuadArgs& args, hipStream_t stream);
+// W4A4 GEMM: Y [M][N] = deq(A) deq(B)^T, A [M][K] and B [N][K] in MXFP4
+// (codes [rows][K/2], E8M0 scales [rows][K/32]); either output may be null.
+struct GemmArgs {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const uint8_t* b_codes;
+  const uint8_t* b_scales;
+  int M, N, K;
+  float* y_f32;
+  uint16_t* y_bf16;
+};
+
+hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream);
 hipError_t launch_row_stats(const uint16_t* X, int T, int d, double eps, float* stats, hipStream_t stream);
-hipError_t launch_build(const float* P, int nb, float* K32, uint16_t* Kbf, int n_split, hipStream_t stream);
+hipError_t launch_build(const float* P, int nb, float* K32, uint16_t* Kbf, int n_split, int inverse_t,
+                        hipStream_t stream);
 
 }  // namespace kq
