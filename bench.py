@@ -202,6 +202,45 @@ def adaln_table(kq, torch, np, synth, dev):
     return out
 
 
+def gemm_table(kq, torch, np, dev):
+    """The W4A4 consumer GEMM (kq_gemm_mx, MXFP4 x MXFP4 -> bf16) at DiT linear-layer shapes:
+    FLUX.1-schnell MLP fc1 / fc2 and attention qkv at 4608 tokens, PixArt-Sigma MLP fc1 at 2 x 4096
+    tokens.  Operands are random codes with scales in [2^-9, 2^6]; the time does not depend on values.
+    TFLOP/s counts 2 M N K; the roofline peak is MI355X's dense FP4 figure, 10.1 PFLOP/s."""
+    out = {}
+    L = kq.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    for name, M, N, K in (("flux_mlp_fc1", 4608, 12288, 3072), ("flux_mlp_fc2", 4608, 3072, 12288),
+                          ("flux_attn_qkv", 4608, 9216, 3072), ("pixart_mlp_fc1", 8192, 4608, 1152)):
+        a = torch.randint(0, 256, (M, K // 2), dtype=torch.uint8, device=dev, generator=g)
+        asc = torch.randint(118, 134, (M, K // 32), dtype=torch.uint8, device=dev, generator=g)
+        b = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=dev, generator=g)
+        bsc = torch.randint(118, 134, (N, K // 32), dtype=torch.uint8, device=dev, generator=g)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        args = (a.data_ptr(), asc.data_ptr(), M, b.data_ptr(), bsc.data_ptr(), N, K, None, y.data_ptr(), stream)
+        t_warm = time.perf_counter() + 0.1
+        while time.perf_counter() < t_warm:
+            for _ in range(5):
+                assert L.kq_gemm_mx(*args) == 0
+            torch.cuda.synchronize()
+        reps = 20
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            L.kq_gemm_mx(*args)
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) * 1e-3 / reps
+        tf = 2.0 * M * N * K / sec / 1e12
+        out[name] = {"M": M, "N": N, "K": K, "us": round(sec * 1e6, 1), "TFLOPs": round(tf, 1),
+                     "frac_fp4_peak": round(tf / 10100.0, 4)}
+        print(f"# gemm {name}: {out[name]}", file=sys.stderr, flush=True)
+    return out
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -212,6 +251,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-shapes", action="store_true", help="skip the per-shape table of the other workloads")
     ap.add_argument("--no-adaln", action="store_true", help="skip the fused AdaLN producer-step table")
+    ap.add_argument("--no-gemm", action="store_true", help="skip the W4A4 GEMM table")
     ap.add_argument("--profile-pass", action="store_true",
                     help="few launches of each kernel plus a plain copy of known size, for rocprofv3 counter runs")
     return ap.parse_args()
@@ -283,6 +323,15 @@ def main():
         kq.kq_smooth_quantize(Xs[0], md, *outs[0])
         kq.kq_mx_quantize(Xs[0], *outs[0])
         kq.kq_hadamard_quantize(Xs[0], *outs[0])
+        # the W4A4 GEMM once at the FLUX MLP fc1 shape
+        gm, gn, gk = 4608, 12288, 3072
+        ga = torch.randint(0, 256, (gm, gk // 2), dtype=torch.uint8, device=dev)
+        gas = torch.full((gm, gk // 32), 127, dtype=torch.uint8, device=dev)
+        gb = torch.randint(0, 256, (gn, gk // 2), dtype=torch.uint8, device=dev)
+        gbs = torch.full((gn, gk // 32), 127, dtype=torch.uint8, device=dev)
+        gy = torch.empty((gm, gn), dtype=torch.bfloat16, device=dev)
+        kq.kq_gemm_mx(ga, gas, gb, gbs, None, gy)
+        del ga, gb, gy
         # plain copy kernel of known size for counter calibration: 1 GiB read + 1 GiB written
         a = torch.empty(1 << 29, dtype=torch.int16, device=dev).fill_(1)
         b = torch.empty_like(a)
@@ -335,6 +384,9 @@ def main():
     adaln = None
     if not args.no_adaln:
         adaln = adaln_table(kq, torch, np, synth, dev)
+    gemm = None
+    if not args.no_gemm:
+        gemm = gemm_table(kq, torch, np, dev)
 
     variant_name = args.variant
     kernel = kq.variant_name(kq.kq_auto_variant(T, d, True, False)) if variant_name == "auto" else variant_name
@@ -367,6 +419,7 @@ def main():
         "comparison": comparison,
         "per_shape": per_shape,
         "adaln_fused": adaln,
+        "w4a4_gemm": gemm,
     }
     print(json.dumps(out), flush=True)
 
