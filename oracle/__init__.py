@@ -65,6 +65,9 @@ def lib():
         L.kqo_dequant_rows.argtypes = [vp, vp, i64, i64, vp]
         L.kqo_quantize_rows_blocks.argtypes = [vp, i64, i64, vp, i64, i64, i64, vp, vp, vp, vp]
         L.kqo_quantize_rows_blocks.restype = ci
+        L.kqo_quantize_rows_hadamard.argtypes = [vp, i64, i64, ci, i64, i64, vp, vp, vp, vp]
+        L.kqo_quantize_rows_hadamard.restype = ci
+        L.kqo_build_blocks16.argtypes = [vp, i64, vp]
         L.kqo_row_stats.argtypes = [vp, i64, i64, d, vp]
         L.kqo_row_stats.restype = ci
         L.kqo_adaln_rows.argtypes = [vp, i64, i64, vp, vp, vp, i64, vp]
@@ -253,6 +256,34 @@ def quantize_rows_blocks(X: np.ndarray, K32: np.ndarray, want_y: bool = False, t
     if want_y:
         out["y32"], out["yhat"] = y32, yhat
     return out
+
+
+def quantize_rows_hadamard(X: np.ndarray, B: int, want_y: bool = False):
+    """Block-Hadamard front-end of size B (32..512) + MXFP4: dict(codes, scales[, y32, yhat])."""
+    X = np.ascontiguousarray(X, dtype=np.uint16)
+    T, d = X.shape
+    out = {"codes": np.zeros((T, d // 2), np.uint8), "scales": np.zeros((T, d // 32), np.uint8)}
+    if want_y:
+        out["y32"] = np.zeros((T, d), np.float32)
+        out["yhat"] = np.zeros((T, d), np.float64)
+    rc = lib().kqo_quantize_rows_hadamard(X.ctypes.data, T, d, int(B), 0, T, out["codes"].ctypes.data,
+                                          out["scales"].ctypes.data,
+                                          out["y32"].ctypes.data if want_y else None,
+                                          out["yhat"].ctypes.data if want_y else None)
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return out
+
+
+def build_blocks16(P16) -> np.ndarray:
+    """16-wide, 4-factor blocks as block-diagonal fp32 32x32 blocks [nb16/2, 32, 32] (P16: [nb16, 4, 3])."""
+    P16 = np.ascontiguousarray(P16, dtype=np.float32)
+    nb16 = P16.shape[0]
+    if nb16 % 2:
+        raise ValueError("nb16 must be even")
+    K = np.empty((nb16 // 2, 32, 32), dtype=np.float32)
+    lib().kqo_build_blocks16(P16.ctypes.data, nb16, K.ctypes.data)
+    return K
 
 
 def dequant_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:

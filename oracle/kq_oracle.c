@@ -419,3 +419,53 @@ int kqo_quantize_rows_blocks(const uint16_t* X, int64_t T, int64_t d, const floa
   }
   return 0;
 }
+
+int kqo_quantize_rows_hadamard(const uint16_t* X, int64_t T, int64_t d, int B, int64_t row0, int64_t row1,
+                               uint8_t* codes, uint8_t* scales, float* y32, double* yhat) {
+  if (!X || !codes || !scales || B < 32 || B > 512 || (B & (B - 1)) || d <= 0 || d % B != 0 || T < 0 || row0 < 0 ||
+      row1 > T || row0 > row1)
+    return 1;
+  const double sqrtB = sqrt((double)B);
+  const int64_t nb = d / 32;
+  double* yh = (double*)malloc(sizeof(double) * (size_t)d);
+  float* y = (float*)malloc(sizeof(float) * (size_t)d);
+  if (!yh || !y) { free(yh); free(y); return 1; }
+  for (int64_t t = row0; t < row1; ++t) {
+    const int64_t ro = t - row0;
+    for (int64_t b0 = 0; b0 < d; b0 += B) {
+      for (int c = 0; c < B; ++c) {
+        double s = 0.0;
+        for (int r = 0; r < B; ++r) {
+          const double x = bf16_to_f64(X[t * d + b0 + r]);
+          s = s + ((__builtin_popcount((unsigned)(r & c)) & 1) ? -x : x);
+        }
+        yh[b0 + c] = s / sqrtB;
+        y[b0 + c] = (float)yh[b0 + c];
+      }
+    }
+    for (int64_t j = 0; j < nb; ++j) kqo_quantize_block(y + 32 * j, codes + ro * (d / 2) + 16 * j, scales + ro * nb + j);
+    if (y32) memcpy(y32 + ro * d, y, sizeof(float) * (size_t)d);
+    if (yhat) memcpy(yhat + ro * d, yh, sizeof(double) * (size_t)d);
+  }
+  free(yh);
+  free(y);
+  return 0;
+}
+
+void kqo_build_blocks16(const float* P, int64_t nb16, float* K32) {
+  for (int64_t j = 0; j < nb16 / 2; ++j) {
+    float* K = K32 + j * 1024;
+    for (int i = 0; i < 1024; ++i) K[i] = 0.0f;
+    for (int h = 0; h < 2; ++h) {
+      double G[4][4];
+      const float* p = P + (2 * j + h) * 12;
+      for (int k = 0; k < 4; ++k) kqo_factor(p[3 * k], p[3 * k + 1], p[3 * k + 2], G[k]);
+      for (int r = 0; r < 16; ++r)
+        for (int cc = 0; cc < 16; ++cc) {
+          double v = G[0][2 * ((r >> 3) & 1) + ((cc >> 3) & 1)];
+          for (int k = 1; k < 4; ++k) v = v * G[k][2 * ((r >> (3 - k)) & 1) + ((cc >> (3 - k)) & 1)];
+          K[(16 * h + r) * 32 + 16 * h + cc] = (float)v;
+        }
+    }
+  }
+}

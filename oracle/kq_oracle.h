@@ -67,6 +67,30 @@ void kqo_build_blocks_inverse_t(const float* P, int64_t nb, int64_t pstride, flo
 int kqo_quantize_rows_blocks(const uint16_t* X, int64_t T, int64_t d, const float* K32, int64_t kstride,
                              int64_t row0, int64_t row1, uint8_t* codes, uint8_t* scales, float* y32, double* yhat);
 
+/*
+ * Fixed block-Hadamard front-end of size B (a power of two, 32 <= B <= 512,
+ * d % B == 0), the "larger block sizes" of the comparison (Pith review,
+ * original abstract; the fixed Hadamard at the block size of the significance
+ * paragraph is B = 32):
+ *   y[c] = RNE_fp32((sum_r x[r] (-1)^popcount(r & c)) / sqrt(B))
+ * over each B-channel block (fp64 sum in input order, one division), then
+ * MXFP4 over blocks of 32 as for every front-end.  B = 32 equals the
+ * KQO_HADAMARD front-end of kqo_quantize_rows.  Returns 0, or 1 on bad args.
+ */
+int kqo_quantize_rows_hadamard(const uint16_t* X, int64_t T, int64_t d, int B, int64_t row0, int64_t row1,
+                               uint8_t* codes, uint8_t* scales, float* y32, double* yhat);
+
+/*
+ * 16-wide KroQuant blocks with four factors (a block-size / factor-count
+ * variant; Pith review, "What carries the argument" and minor comments): for
+ * each 16-channel block b the 16x16 matrix G1 (x) G2 (x) G3 (x) G4 (G1 on bit
+ * 3 of the index, 12 scalars at P + 12 b), each entry the fp64 product in
+ * factor order rounded once to fp32.  Written as block-diagonal 32x32 fp32
+ * blocks diag(K_{2j}, K_{2j+1}) into K32 [nb16/2][32][32] (zeros elsewhere),
+ * ready for kqo_quantize_rows_blocks; nb16 must be even.
+ */
+void kqo_build_blocks16(const float* P, int64_t nb16, float* K32);
+
 /* MXFP4 dequantization: out[t][c] = E2M1(code) * 2^(scale - 127) in fp64 ([n][d]). */
 void kqo_dequant_rows(const uint8_t* codes, const uint8_t* scales, int64_t n, int64_t d, double* out);
 
