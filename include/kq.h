@@ -104,7 +104,7 @@ typedef enum {
 typedef enum { KQ_FRONT_KRON = 0, KQ_FRONT_PLAIN = 1, KQ_FRONT_SMOOTH = 2, KQ_FRONT_HADAMARD = 3 } kq_front;
 
 /* ABI version of this header (bumped on any signature or layout change). */
-#define KQ_ABI_VERSION 3
+#define KQ_ABI_VERSION 4
 int kq_abi_version(void);
 
 /* Static, never-NULL description of a status code. */
@@ -172,6 +172,29 @@ kq_status kq_smooth_quantize(const uint16_t* X, int64_t tokens, int64_t d, const
  */
 kq_status kq_hadamard_quantize(const uint16_t* X, int64_t tokens, int64_t d, uint8_t* out_codes,
                                uint8_t* out_scales, hipStream_t stream);
+
+/*
+ * Block-Hadamard front-end of size `block` (32, 64, 128, 256 or 512; d a
+ * multiple of it) then MXFP4 over blocks of 32: y[c] = fp32(sum_r x[r]
+ * H[r][c] / sqrt(block)) within each block of `block` channels, the "larger
+ * block sizes" a fixed Hadamard needs (Pith review, original abstract).
+ * block = 32 is kq_hadamard_quantize.  Other sizes -> KQ_ERR_SHAPE.
+ */
+kq_status kq_hadamard_quantize_ex(const uint16_t* X, int64_t tokens, int64_t d, int block, uint8_t* out_codes,
+                                  uint8_t* out_scales, hipStream_t stream);
+
+/*
+ * 16-wide KroQuant blocks with four factors (a block-size / factor-count
+ * variant, 12 scalars per 16 channels at K_params16 + 12 b, (l, a, b) of
+ * G1 .. G4, G1 on bit 3 of the 16-index): written as block-diagonal 32x32
+ * blocks diag(K_{2j}, K_{2j+1}) in the layouts of kq_build_blocks (K_f32
+ * [nb16/2][32][32], K_bf16 [nb16/2][n_split][32][32] transposed), each entry
+ * the fp64 product in factor order rounded once to fp32, zeros off the
+ * diagonal blocks.  Quantize with kq_quantize_ex(..., K_bf16, KQ_MFMA_DENSE).
+ * nb16 must be even (KQ_ERR_SHAPE otherwise); errors as kq_build_blocks.
+ */
+kq_status kq_build_blocks16(const float* K_params16, int64_t nb16, float* K_f32, uint16_t* K_bf16, int n_split,
+                            hipStream_t stream);
 
 /*
  * Diagnostic entry (tests): runs the same kernels as the entries above and

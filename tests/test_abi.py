@@ -170,3 +170,23 @@ def test_quantize_adaln_argument_checks(lib):
     # an output overlapping the statistics or a modulation vector
     assert q(A, 100, 64, B, C, D, 64, E, 15, None, 0, B + 64, G, None) == KQ_ERR_ALIAS
     assert q(A, 100, 64, B, C, D, 64, E, 15, None, 0, F, D + 16, None) == KQ_ERR_ALIAS
+
+
+def test_variant_entry_checks(lib):
+    vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.kq_hadamard_quantize_ex.argtypes = [vp, i64, i64, ci, vp, vp, vp]
+    lib.kq_build_blocks16.argtypes = [vp, i64, vp, vp, ci, vp]
+    h = lib.kq_hadamard_quantize_ex
+    for block in (16, 48, 1024, 0, -32):
+        assert h(A, 4, 1024, block, C, D, None) == KQ_ERR_SHAPE
+    assert h(A, 4, 1152, 256, C, D, None) == KQ_ERR_SHAPE  # d not a multiple of the block
+    assert h(A, 0, 1024, 512, None, None, None) == KQ_OK
+    assert h(None, 4, 1024, 512, C, D, None) == KQ_ERR_NULL
+    b = lib.kq_build_blocks16
+    assert b(A, 3, B, None, 3, None) == KQ_ERR_SHAPE  # odd block count
+    assert b(A, 0, B, None, 3, None) == KQ_ERR_SHAPE
+    assert b(A, 4, None, C, 4, None) == KQ_ERR_SHAPE
+    assert b(None, 4, B, None, 3, None) == KQ_ERR_NULL
+    assert b(A, 4, None, None, 3, None) == KQ_ERR_NULL
+    assert b(A + 2, 4, B, None, 3, None) == KQ_ERR_ALIGN
+    assert b(A, 4, A + 64, None, 3, None) == KQ_ERR_ALIAS

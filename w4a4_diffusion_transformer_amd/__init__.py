@@ -20,7 +20,7 @@ __all__ = [
     "lib", "kq_abi_version", "kq_status_str", "kq_build_blocks", "kq_quantize", "kq_quantize_ex",
     "kq_mx_quantize", "kq_smooth_quantize", "kq_hadamard_quantize", "kq_transform_f32",
     "alloc_outputs", "LIB_PATH", "kq_auto_variant", "variant_name", "kq_row_stats", "kq_quantize_adaln",
-    "kq_build_blocks_inverse_t", "kq_gemm_mx",
+    "kq_build_blocks_inverse_t", "kq_gemm_mx", "kq_hadamard_quantize_ex", "kq_build_blocks16",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkq.so")
@@ -62,10 +62,12 @@ def lib() -> ctypes.CDLL:
         L.kq_row_stats.argtypes = [vp, i64, i64, ctypes.c_float, vp, vp]
         L.kq_build_blocks_inverse_t.argtypes = [vp, i64, vp, vp, ci, vp]
         L.kq_gemm_mx.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, vp, vp]
+        L.kq_hadamard_quantize_ex.argtypes = [vp, i64, i64, ci, vp, vp, vp]
+        L.kq_build_blocks16.argtypes = [vp, i64, vp, vp, ci, vp]
         L.kq_quantize_adaln.argtypes = [vp, i64, i64, vp, vp, vp, i64, vp, i64, vp, ci, vp, vp, vp]
         for name in ("kq_build_blocks", "kq_quantize", "kq_quantize_ex", "kq_mx_quantize", "kq_smooth_quantize",
                      "kq_hadamard_quantize", "kq_transform_f32", "kq_row_stats", "kq_quantize_adaln",
-                     "kq_build_blocks_inverse_t", "kq_gemm_mx"):
+                     "kq_build_blocks_inverse_t", "kq_gemm_mx", "kq_hadamard_quantize_ex", "kq_build_blocks16"):
             getattr(L, name).restype = ci
         _lib = L
     return _lib
@@ -232,3 +234,18 @@ def kq_gemm_mx(a_codes, a_scales, b_codes, b_scales, y_f32=None, y_bf16=None, st
                             _ptr(y_f32, "y_f32", _F32), _ptr(y_bf16, "y_bf16", _BF16), _stream(stream)),
            "kq_gemm_mx")
     return y_f32, y_bf16
+
+
+def kq_hadamard_quantize_ex(X, block: int, out_codes, out_scales, stream=None):
+    """Block-Hadamard (size 32..512) front-end + MXFP4."""
+    T, d = _shape(X)
+    _check(lib().kq_hadamard_quantize_ex(_ptr(X, "X", _BF16), T, d, int(block), _ptr(out_codes, "out_codes", _U8),
+                                         _ptr(out_scales, "out_scales", _U8), _stream(stream)), "kq_hadamard_quantize_ex")
+    return out_codes, out_scales
+
+
+def kq_build_blocks16(K_params16, nb16: int, K_f32=None, K_bf16=None, n_split: int = 3, stream=None):
+    """16-wide 4-factor blocks as block-diagonal 32x32 dense blocks (fp32 and/or transposed bf16 split)."""
+    _check(lib().kq_build_blocks16(_ptr(K_params16, "K_params16", _F32), nb16, _ptr(K_f32, "K_f32", _F32),
+                                   _ptr(K_bf16, "K_bf16", _BF16), n_split, _stream(stream)), "kq_build_blocks16")
+    return K_f32, K_bf16

@@ -4,6 +4,7 @@
 
 #include <atomic>
 #include <cstdlib>
+#include <cmath>
 #include <cstring>
 #include <mutex>
 
@@ -95,12 +96,15 @@ struct Mod {
 
 kq_status run(int front, const uint16_t* X, int64_t tokens, int64_t d, const float* P, int64_t pstride,
               const uint16_t* Kbf, int variant, const float* m, float* Y, uint8_t* codes, uint8_t* scales,
-              hipStream_t stream, const Mod* mod = nullptr) {
+              hipStream_t stream, const Mod* mod = nullptr, int hblock = 32) {
   kq_status st = check_shape(tokens, d);
   if (st != KQ_OK) return st;
   if (front < kq::FRONT_KRON || front > kq::FRONT_HADAMARD) return KQ_ERR_VARIANT;
   if (variant < KQ_AUTO || variant > KQ_BUTTERFLY) return KQ_ERR_VARIANT;
   if (front == kq::FRONT_KRON && pstride != 15 && pstride != 0) return KQ_ERR_SHAPE;
+  if (front == kq::FRONT_HADAMARD &&
+      (hblock < 32 || hblock > 512 || (hblock & (hblock - 1)) != 0 || d % hblock != 0))
+    return KQ_ERR_SHAPE;
   if (mod) {
     // a tile of 32 rows never straddles two samples
     if (mod->tps <= 0 || (mod->tps % 32 != 0 && mod->tps < tokens)) return KQ_ERR_SHAPE;
@@ -160,6 +164,9 @@ kq_status run(int front, const uint16_t* X, int64_t tokens, int64_t d, const flo
         kq::launch_mfma(variant == KQ_MFMA_OTF ? KSRC_PARAMS : KSRC_SPLIT, Y != nullptr, mod != nullptr, a, stream));
   }
   kq::QuadArgs a{};
+  a.hlog = 5;
+  while ((1 << a.hlog) < hblock) ++a.hlog;
+  a.hscale = (float)(1.0 / std::sqrt((double)hblock));
   a.X = X;
   a.T = T;
   a.d = (int)d;
@@ -300,6 +307,26 @@ kq_status kq_hadamard_quantize(const uint16_t* X, int64_t tokens, int64_t d, uin
                                uint8_t* out_scales, hipStream_t stream) {
   return run(kq::FRONT_HADAMARD, X, tokens, d, nullptr, 15, nullptr, KQ_AUTO, nullptr, nullptr, out_codes,
              out_scales, stream);
+}
+
+kq_status kq_hadamard_quantize_ex(const uint16_t* X, int64_t tokens, int64_t d, int block, uint8_t* out_codes,
+                                  uint8_t* out_scales, hipStream_t stream) {
+  return run(kq::FRONT_HADAMARD, X, tokens, d, nullptr, 15, nullptr, KQ_AUTO, nullptr, nullptr, out_codes,
+             out_scales, stream, nullptr, block);
+}
+
+kq_status kq_build_blocks16(const float* K_params16, int64_t nb16, float* K_f32, uint16_t* K_bf16, int n_split,
+                            hipStream_t stream) {
+  if (nb16 <= 0 || nb16 % 2 != 0 || nb16 >= (int64_t(1) << 21)) return KQ_ERR_SHAPE;
+  if (K_bf16 && (n_split < 1 || n_split > 3)) return KQ_ERR_SHAPE;
+  if (!K_params16 || (!K_f32 && !K_bf16)) return KQ_ERR_NULL;
+  if (!aligned(K_params16, 4) || (K_f32 && !aligned(K_f32, 4)) || (K_bf16 && !aligned(K_bf16, 16)))
+    return KQ_ERR_ALIGN;
+  const uint64_t nb = (uint64_t)nb16 / 2;
+  const Range outs[] = {{K_f32, nb * 4096}, {K_bf16, K_bf16 ? nb * 2048 * (uint64_t)n_split : 0}};
+  const Range ins[] = {{K_params16, (uint64_t)nb16 * 48}};
+  if (any_alias(outs, 2, ins, 1)) return KQ_ERR_ALIAS;
+  return from_hip(kq::launch_build16(K_params16, (int)nb, K_f32, K_bf16, K_bf16 ? n_split : 0, stream));
 }
 
 kq_status kq_transform_f32(int front, const uint16_t* X, int64_t tokens, int64_t d, const float* K_params,

@@ -40,7 +40,44 @@ __global__ __launch_bounds__(256) void build_kernel(const float* __restrict__ P,
   }
 }
 
+// 16-wide blocks with four factors, as block-diagonal 32x32 blocks: entry
+// [r][c] of block j is zero unless r and c lie in the same half h; then it is
+// the fp64 product in factor order of G1 .. G4 of 16-wide block 2 j + h (G1 on
+// bit 3 of r & 15 and c & 15), rounded once to fp32.
+__global__ __launch_bounds__(256) void build16_kernel(const float* __restrict__ P, int nb, float* __restrict__ K32,
+                                                      uint16_t* __restrict__ Kbf, int n_split) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)nb * 1024) return;
+  const int j = (int)(idx >> 10), r = (int)((idx >> 5) & 31), c = (int)(idx & 31);
+  float k = 0.0f;
+  if ((r >> 4) == (c >> 4)) {
+    const float* p = P + (int64_t)(2 * j + (r >> 4)) * 12;
+    const Factor f1 = factor_f64(p), f2 = factor_f64(p + 3), f3 = factor_f64(p + 6), f4 = factor_f64(p + 9);
+    double v = pick(f1, (r >> 3) & 1, (c >> 3) & 1);
+    v = v * pick(f2, (r >> 2) & 1, (c >> 2) & 1);
+    v = v * pick(f3, (r >> 1) & 1, (c >> 1) & 1);
+    v = v * pick(f4, r & 1, c & 1);
+    k = (float)v;
+  }
+  if (K32) K32[idx] = k;
+  if (Kbf) {
+    float rest = k;
+    for (int s = 0; s < n_split; ++s) {
+      const __bf16 h = (__bf16)rest;
+      Kbf[(((int64_t)j * n_split + s) * 32 + c) * 32 + r] = __builtin_bit_cast(uint16_t, h);
+      rest = rest - (float)h;
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_build16(const float* P16, int nb, float* K32, uint16_t* Kbf, int n_split, hipStream_t stream) {
+  const int64_t n = (int64_t)nb * 1024;
+  const int grid = (int)((n + 255) / 256);
+  void* kargs[] = {&P16, &nb, &K32, &Kbf, &n_split};
+  return hipLaunchKernel((const void*)&build16_kernel, dim3(grid), dim3(256), kargs, 0, stream);
+}
 
 hipError_t launch_build(const float* P, int nb, float* K32, uint16_t* Kbf, int n_split, int inverse_t,
                         hipStream_t stream) {

@@ -184,6 +184,31 @@ struct ExactHadamard {
   }
 };
 
+// Block-Hadamard column for block sizes B = 32 .. 512: the same fp64 sum over
+// the B inputs of the Hadamard block (input order), divided once by sqrt(B).
+// xB points at the B-block's first input, off is this 32-block's offset in it.
+struct ExactHadamardB {
+  const uint16_t* xB;
+  int B;
+  int off;
+  __device__ float operator()(const uint16_t* __restrict__, int c) const {
+    const int col = off + c;
+    double s = 0.0;
+#pragma unroll 1
+    for (int r = 0; r < B; ++r) {
+      const double x = (double)__uint_as_float((unsigned)xB[r] << 16);
+      s = s + ((__popc(r & col) & 1) ? -x : x);
+    }
+    // sqrt(B) for B = 32, 64, 128, 256, 512, each correctly rounded
+    const double sq = B == 32    ? 5.6568542494923801952067548968387923142786875015078
+                      : B == 64  ? 8.0
+                      : B == 128 ? 11.313708498984760390413509793677584628557375003016
+                      : B == 256 ? 16.0
+                                 : 22.627416997969520780827019587355169257114750006031;
+    return (float)(s / sq);
+  }
+};
+
 // ---------------------------------------------------------------- epilogue
 //
 // MXFP4 for one lane's 8 values of a block whose four lanes hold one token:

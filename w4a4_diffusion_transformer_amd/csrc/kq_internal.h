@@ -51,6 +51,8 @@ struct QuadArgs {
   uint8_t* codes;
   uint8_t* scales;
   float* Y;
+  int hlog;        // Hadamard front-end: log2 of the block size (5 .. 9)
+  float hscale;    // and 1 / sqrt(block size) in fp32
   int ngroups, nchunks;
 };
 
@@ -82,5 +84,6 @@ hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream);
 hipError_t launch_row_stats(const uint16_t* X, int T, int d, double eps, float* stats, hipStream_t stream);
 hipError_t launch_build(const float* P, int nb, float* K32, uint16_t* Kbf, int n_split, int inverse_t,
                         hipStream_t stream);
+hipError_t launch_build16(const float* P16, int nb, float* K32, uint16_t* Kbf, int n_split, hipStream_t stream);
 
 }  // namespace kq

@@ -6,7 +6,9 @@
 //                   review, "What carries the argument");
 //   FRONT_PLAIN     y = x;
 //   FRONT_SMOOTH    y = x * m[c] (SmoothQuant per-channel scale);
-//   FRONT_HADAMARD  y = (x H32)[c] / sqrt(32), fast Walsh-Hadamard butterflies.
+//   FRONT_HADAMARD  y = (x H_B)[c] / sqrt(B), fast Walsh-Hadamard butterflies
+//                   over blocks of B = 32 .. 512 channels (stages on channel
+//                   bits 5 and up pair lanes 4, 8, 16, 32 apart).
 //
 // Lane layout: a wave covers 1 KB of one bf16 row (16 blocks); lane l owns
 // the fixed 16-byte piece l, i.e. channels 8q .. 8q+7 (q = l & 3) of block
@@ -139,7 +141,6 @@ __global__ __launch_bounds__(64 * kWaves) void quad_kernel(QuadArgs a) {
     }
   }
   const float sgn3 = (q & 1) ? -1.0f : 1.0f, sgn4 = (q >> 1) ? -1.0f : 1.0f;
-  constexpr float kInvSqrt32 = 0.17677669529663688110f;
 
   const int64_t d = a.d;
   const int nrb = (a.T + kWaves - 1) / kWaves;  // row blocks of kWaves rows
@@ -193,8 +194,16 @@ __global__ __launch_bounds__(64 * kWaves) void quad_kernel(QuadArgs a) {
       wht_in_reg<4>(y);
       wht_cross<1>(y, sgn3);
       wht_cross<2>(y, sgn4);
+      // channel bits 5 .. hlog-1 (blocks of 64 .. 512): bit b of the channel is bit b-3 of the lane
+#pragma unroll 1
+      for (int bt = 5; bt < a.hlog; ++bt) {
+        const int m = 1 << (bt - 3);
+        const float sgn = (lane & m) ? -1.0f : 1.0f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) y[i] *= kInvSqrt32;
+        for (int i = 0; i < 8; ++i) y[i] = fmaf(y[i], sgn, __shfl_xor(y[i], m, 64));
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] *= a.hscale;
     }
     // rows past the end hold zeros (amax 0): the exact path never runs for them
     const uint16_t* xblk = (in ? cx : a.X) + 32 * jc;
@@ -202,7 +211,9 @@ __global__ __launch_bounds__(64 * kWaves) void quad_kernel(QuadArgs a) {
     if constexpr (FRONT == FRONT_KRON) {
       mx_epilogue<LAYOUT_QUAD, true>(y, xblk, q, ExactFromFactors{lds_g[lane >> 2]}, word, byte);
     } else if constexpr (FRONT == FRONT_HADAMARD) {
-      mx_epilogue<LAYOUT_QUAD, true>(y, xblk, q, ExactHadamard{}, word, byte);
+      const int hb = 1 << a.hlog;
+      const int off = (32 * jc) & (hb - 1);
+      mx_epilogue<LAYOUT_QUAD, true>(y, xblk, q, ExactHadamardB{xblk - off, hb, off}, word, byte);
     } else {
       mx_epilogue<LAYOUT_QUAD, false>(y, xblk, q, NoExact{}, word, byte);
     }
