@@ -92,7 +92,7 @@ typedef enum {
   KQ_ERR_ALIAS = 6
 } kq_status;
 
-/* How K is applied.  AUTO picks per shape (documented in kq_api.hip). */
+/* How K is applied.  AUTO picks per shape: a kq_tune result if one was recorded, else the rule in kq_auto_variant. */
 typedef enum {
   KQ_AUTO = 0,
   KQ_MFMA_DENSE = 1, /* MFMA bf16 contraction with prebuilt K_bf16 (three-term split) */
@@ -104,7 +104,7 @@ typedef enum {
 typedef enum { KQ_FRONT_KRON = 0, KQ_FRONT_PLAIN = 1, KQ_FRONT_SMOOTH = 2, KQ_FRONT_HADAMARD = 3 } kq_front;
 
 /* ABI version of this header (bumped on any signature or layout change). */
-#define KQ_ABI_VERSION 4
+#define KQ_ABI_VERSION 5
 int kq_abi_version(void);
 
 /* Static, never-NULL description of a status code. */
@@ -195,6 +195,25 @@ kq_status kq_hadamard_quantize_ex(const uint16_t* X, int64_t tokens, int64_t d, 
  */
 kq_status kq_build_blocks16(const float* K_params16, int64_t nb16, float* K_f32, uint16_t* K_bf16, int n_split,
                             hipStream_t stream);
+
+/*
+ * Per-shape tuning of KQ_AUTO (opt-in).  Times every variant the supplied
+ * inputs allow (KQ_MFMA_OTF and KQ_BUTTERFLY need K_params with stride 15,
+ * KQ_MFMA_DENSE needs K_bf16) on the caller's buffers: 3 warm-up launches and
+ * `reps` timed launches each (1 <= reps <= 1000, else KQ_ERR_SHAPE), timed
+ * with events on `stream`.  The fastest is recorded for (tokens, d, which
+ * inputs are supplied), process-wide, and later KQ_AUTO calls with that key
+ * use it (kq_auto_variant reports it; a KQ_VARIANT environment override still
+ * wins).  On return out_codes / out_scales hold the chosen variant's result
+ * and *chosen (if not NULL) the variant.  This is the one entry point that
+ * blocks: it synchronizes on its timing event.  Neither input -> KQ_ERR_VARIANT;
+ * other errors as kq_quantize_ex; a failed launch or event -> KQ_ERR_HIP.
+ */
+kq_status kq_tune(const uint16_t* X, int64_t tokens, int64_t d, const float* K_params, const uint16_t* K_bf16,
+                  uint8_t* out_codes, uint8_t* out_scales, int reps, kq_variant* chosen, hipStream_t stream);
+
+/* Forget every choice kq_tune recorded (KQ_AUTO falls back to its default rule). */
+void kq_tune_reset(void);
 
 /*
  * Diagnostic entry (tests): runs the same kernels as the entries above and

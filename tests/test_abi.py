@@ -190,3 +190,20 @@ def test_variant_entry_checks(lib):
     assert b(A, 4, None, None, 3, None) == KQ_ERR_NULL
     assert b(A + 2, 4, B, None, 3, None) == KQ_ERR_ALIGN
     assert b(A, 4, A + 64, None, 3, None) == KQ_ERR_ALIAS
+
+
+def test_tune_argument_checks(lib):
+    vp, i64, ci = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.kq_tune.argtypes = [vp, i64, i64, vp, vp, vp, vp, ci, ctypes.POINTER(ci), vp]
+    lib.kq_tune_reset.restype = None
+    chosen = ctypes.c_int(-1)
+    t = lib.kq_tune
+    assert t(A, 4, 48, B, None, C, D, 5, ctypes.byref(chosen), None) == KQ_ERR_SHAPE
+    assert t(A, 4, 64, B, None, C, D, 0, ctypes.byref(chosen), None) == KQ_ERR_SHAPE
+    assert t(A, 4, 64, None, None, C, D, 5, ctypes.byref(chosen), None) == KQ_ERR_VARIANT
+    assert t(None, 4, 64, B, None, C, D, 5, ctypes.byref(chosen), None) == KQ_ERR_NULL
+    assert t(A + 2, 4, 64, B, None, C, D, 5, ctypes.byref(chosen), None) == KQ_ERR_ALIGN
+    assert t(A, 4, 64, B, None, A + 16, D, 5, ctypes.byref(chosen), None) == KQ_ERR_ALIAS
+    assert t(A, 0, 64, B, None, C, D, 5, ctypes.byref(chosen), None) == KQ_OK
+    assert chosen.value == 2  # no tuning recorded: the default rule (mfma_otf)
+    lib.kq_tune_reset()

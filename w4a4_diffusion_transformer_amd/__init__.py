@@ -20,7 +20,8 @@ __all__ = [
     "lib", "kq_abi_version", "kq_status_str", "kq_build_blocks", "kq_quantize", "kq_quantize_ex",
     "kq_mx_quantize", "kq_smooth_quantize", "kq_hadamard_quantize", "kq_transform_f32",
     "alloc_outputs", "LIB_PATH", "kq_auto_variant", "variant_name", "kq_row_stats", "kq_quantize_adaln",
-    "kq_build_blocks_inverse_t", "kq_gemm_mx", "kq_hadamard_quantize_ex", "kq_build_blocks16",
+    "kq_build_blocks_inverse_t", "kq_gemm_mx", "kq_hadamard_quantize_ex", "kq_build_blocks16", "kq_tune",
+    "kq_tune_reset",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkq.so")
@@ -64,10 +65,13 @@ def lib() -> ctypes.CDLL:
         L.kq_gemm_mx.argtypes = [vp, vp, i64, vp, vp, i64, i64, vp, vp, vp]
         L.kq_hadamard_quantize_ex.argtypes = [vp, i64, i64, ci, vp, vp, vp]
         L.kq_build_blocks16.argtypes = [vp, i64, vp, vp, ci, vp]
+        L.kq_tune.argtypes = [vp, i64, i64, vp, vp, vp, vp, ci, ctypes.POINTER(ci), vp]
+        L.kq_tune_reset.argtypes = []
+        L.kq_tune_reset.restype = None
         L.kq_quantize_adaln.argtypes = [vp, i64, i64, vp, vp, vp, i64, vp, i64, vp, ci, vp, vp, vp]
         for name in ("kq_build_blocks", "kq_quantize", "kq_quantize_ex", "kq_mx_quantize", "kq_smooth_quantize",
                      "kq_hadamard_quantize", "kq_transform_f32", "kq_row_stats", "kq_quantize_adaln",
-                     "kq_build_blocks_inverse_t", "kq_gemm_mx", "kq_hadamard_quantize_ex", "kq_build_blocks16"):
+                     "kq_build_blocks_inverse_t", "kq_gemm_mx", "kq_hadamard_quantize_ex", "kq_build_blocks16", "kq_tune"):
             getattr(L, name).restype = ci
         _lib = L
     return _lib
@@ -249,3 +253,17 @@ def kq_build_blocks16(K_params16, nb16: int, K_f32=None, K_bf16=None, n_split: i
     _check(lib().kq_build_blocks16(_ptr(K_params16, "K_params16", _F32), nb16, _ptr(K_f32, "K_f32", _F32),
                                    _ptr(K_bf16, "K_bf16", _BF16), n_split, _stream(stream)), "kq_build_blocks16")
     return K_f32, K_bf16
+
+
+def kq_tune(X, K_params, K_bf16, out_codes, out_scales, reps: int = 10, stream=None) -> int:
+    """Time the variants the inputs allow, record the fastest for KQ_AUTO at this shape; returns it."""
+    T, d = _shape(X)
+    chosen = ctypes.c_int(0)
+    _check(lib().kq_tune(_ptr(X, "X", _BF16), T, d, _ptr(K_params, "K_params", _F32), _ptr(K_bf16, "K_bf16", _BF16),
+                         _ptr(out_codes, "out_codes", _U8), _ptr(out_scales, "out_scales", _U8), int(reps),
+                         ctypes.byref(chosen), _stream(stream)), "kq_tune")
+    return chosen.value
+
+
+def kq_tune_reset() -> None:
+    lib().kq_tune_reset()

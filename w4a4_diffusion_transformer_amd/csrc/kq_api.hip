@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "kq.h"
 #include "kq_device.hpp"
@@ -65,13 +66,50 @@ const Overrides& overrides() {
   return o;
 }
 
-// KQ_AUTO: the MFMA kernel with K rebuilt in-kernel measured fastest on
-// MI355X at the DiT widths (it needs only the 60-byte parameter sets); the
-// dense-block MFMA kernel when only prebuilt blocks are given.  KQ_VARIANT
-// overrides the choice when its inputs are present.
-int auto_variant(int64_t, int64_t, bool has_params, bool has_split) {
+// Choices recorded by kq_tune, keyed by shape and the inputs supplied.
+struct Tuned {
+  int64_t tokens, d;
+  bool has_params, has_split;
+  int variant;
+};
+
+std::mutex& tuned_mutex() {
+  static std::mutex mu;
+  return mu;
+}
+
+std::vector<Tuned>& tuned_table() {
+  static std::vector<Tuned> table;
+  return table;
+}
+
+int tuned_lookup(int64_t tokens, int64_t d, bool has_params, bool has_split) {
+  std::lock_guard<std::mutex> lock(tuned_mutex());
+  for (const Tuned& t : tuned_table())
+    if (t.tokens == tokens && t.d == d && t.has_params == has_params && t.has_split == has_split) return t.variant;
+  return KQ_AUTO;
+}
+
+void tuned_store(int64_t tokens, int64_t d, bool has_params, bool has_split, int variant) {
+  std::lock_guard<std::mutex> lock(tuned_mutex());
+  for (Tuned& t : tuned_table())
+    if (t.tokens == tokens && t.d == d && t.has_params == has_params && t.has_split == has_split) {
+      t.variant = variant;
+      return;
+    }
+  tuned_table().push_back(Tuned{tokens, d, has_params, has_split, variant});
+}
+
+// KQ_AUTO: a KQ_VARIANT override when its inputs are present; else the
+// variant kq_tune measured fastest for this shape and these inputs; else the
+// MFMA kernel with K rebuilt in-kernel, measured fastest on MI355X at the DiT
+// widths (it needs only the 60-byte parameter sets), or the dense-block MFMA
+// kernel when only prebuilt blocks are given.
+int auto_variant(int64_t tokens, int64_t d, bool has_params, bool has_split) {
   const int o = overrides().variant;
   if (o > 0 && (o == KQ_MFMA_DENSE ? has_split : has_params)) return o;
+  const int t = tuned_lookup(tokens, d, has_params, has_split);
+  if (t != KQ_AUTO) return t;
   if (has_params) return KQ_MFMA_OTF;
   if (has_split) return KQ_MFMA_DENSE;
   return KQ_AUTO;
@@ -96,7 +134,7 @@ struct Mod {
 
 kq_status run(int front, const uint16_t* X, int64_t tokens, int64_t d, const float* P, int64_t pstride,
               const uint16_t* Kbf, int variant, const float* m, float* Y, uint8_t* codes, uint8_t* scales,
-              hipStream_t stream, const Mod* mod = nullptr, int hblock = 32) {
+              hipStream_t stream, const Mod* mod = nullptr, int hblock = 32, bool check_only = false) {
   kq_status st = check_shape(tokens, d);
   if (st != KQ_OK) return st;
   if (front < kq::FRONT_KRON || front > kq::FRONT_HADAMARD) return KQ_ERR_VARIANT;
@@ -139,6 +177,7 @@ kq_status run(int front, const uint16_t* X, int64_t tokens, int64_t d, const flo
                        {mod ? mod->mscale : nullptr, nsamples * (uint64_t)d * 4},
                        {mod ? mod->mshift : nullptr, nsamples * (uint64_t)d * 4}};
   if (any_alias(outs, 3, ins, 7)) return KQ_ERR_ALIAS;
+  if (check_only) return KQ_OK;
 
   const int T = (int)tokens;
   if (front == kq::FRONT_KRON && variant != KQ_BUTTERFLY) {
@@ -380,6 +419,72 @@ kq_status kq_gemm_mx(const uint8_t* A_codes, const uint8_t* A_scales, int64_t M,
   if (any_alias(outs, 2, ins, 4)) return KQ_ERR_ALIAS;
   kq::GemmArgs g{A_codes, A_scales, B_codes, B_scales, (int)M, (int)N, (int)K, Y_f32, Y_bf16};
   return from_hip(kq::launch_gemm(g, stream));
+}
+
+kq_status kq_tune(const uint16_t* X, int64_t tokens, int64_t d, const float* K_params, const uint16_t* K_bf16,
+                  uint8_t* out_codes, uint8_t* out_scales, int reps, kq_variant* chosen, hipStream_t stream) {
+  kq_status st = check_shape(tokens, d);
+  if (st != KQ_OK) return st;
+  if (reps < 1 || reps > 1000) return KQ_ERR_SHAPE;
+  if (!K_params && !K_bf16) return KQ_ERR_VARIANT;
+  if (tokens == 0) {
+    if (chosen) *chosen = (kq_variant)auto_variant(tokens, d, K_params != nullptr, K_bf16 != nullptr);
+    return KQ_OK;
+  }
+  int cands[3];
+  int nc = 0;
+  if (K_params) cands[nc++] = KQ_MFMA_OTF;
+  if (K_bf16) cands[nc++] = KQ_MFMA_DENSE;
+  if (K_params) cands[nc++] = KQ_BUTTERFLY;
+  // argument checks of every candidate before any HIP call
+  for (int i = 0; i < nc; ++i) {
+    st = run(kq::FRONT_KRON, X, tokens, d, K_params, 15, K_bf16, cands[i], nullptr, nullptr, out_codes, out_scales,
+             stream, nullptr, 32, true);
+    if (st != KQ_OK) return st;
+  }
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess) return KQ_ERR_HIP;
+  if (hipEventCreate(&e1) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    return KQ_ERR_HIP;
+  }
+  int best = cands[0];
+  float best_ms = 0.0f;
+  st = KQ_OK;
+  for (int i = 0; i < nc && st == KQ_OK; ++i) {
+    auto once = [&]() {
+      return run(kq::FRONT_KRON, X, tokens, d, K_params, 15, K_bf16, cands[i], nullptr, nullptr, out_codes, out_scales,
+                 stream);
+    };
+    for (int w = 0; w < 3 && st == KQ_OK; ++w) st = once();  // warm-up
+    if (st != KQ_OK) break;
+    if (hipEventRecord(e0, stream) != hipSuccess) { st = KQ_ERR_HIP; break; }
+    for (int r = 0; r < reps && st == KQ_OK; ++r) st = once();
+    if (st != KQ_OK) break;
+    float ms = 0.0f;
+    if (hipEventRecord(e1, stream) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+        hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+      st = KQ_ERR_HIP;
+      break;
+    }
+    if (i == 0 || ms < best_ms) {
+      best = cands[i];
+      best_ms = ms;
+    }
+  }
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (st != KQ_OK) return st;
+  tuned_store(tokens, d, K_params != nullptr, K_bf16 != nullptr, best);
+  if (chosen) *chosen = (kq_variant)best;
+  // leave the chosen variant's result in the outputs
+  return run(kq::FRONT_KRON, X, tokens, d, K_params, 15, K_bf16, best, nullptr, nullptr, out_codes, out_scales,
+             stream);
+}
+
+void kq_tune_reset(void) {
+  std::lock_guard<std::mutex> lock(tuned_mutex());
+  tuned_table().clear();
 }
 
 }  // extern "C"
