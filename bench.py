@@ -27,7 +27,7 @@ METRIC = "transform+MXFP4 quantize GB/s and % of MI355X HBM peak; Gelem/s per sh
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD public specification
 BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0
 CALLS = 57
-KERNEL_SOURCES = ["kq_device.hpp", "kq_mfma.hip", "kq_quad.hip", "kq_api.hip"]
+KERNEL_SOURCES = ["kq_device.hpp", "kq_mfma.hip"]  # the dominant kernel (mfma_kernel) and its device helpers
 
 
 def kernel_source_hash() -> str:
@@ -94,6 +94,13 @@ def shape_table(kq, torch, np, synth, dev):
             calls["plain"] = (L.kq_mx_quantize, lambda i: (xs[i], T, d, *os_[i], stream))
             calls["hadamard32"] = (L.kq_hadamard_quantize, lambda i: (xs[i], T, d, *os_[i], stream))
         row = {"T": T, "d": d}
+        if not spec.shared_k:
+            # kq_tune's pick for this shape (K_params and the dense split both supplied; kq_tune takes
+            # per-block parameters only), then timed through KQ_AUTO
+            tuned = kq.kq_tune(Xs[0], Pd, Kbf, *outs[0], reps=10)
+            row["tuned_variant"] = kq.variant_name(tuned)
+            calls["kroquant_tuned"] = (L.kq_quantize_ex,
+                                       lambda i: (xs[i], T, d, pp, 15, kp, kq.KQ_AUTO, *os_[i], stream))
         for name, (fn, mk) in calls.items():
             argv = [mk(i) for i in range(copies)]
             reps = max(60, 4 * copies)
@@ -115,6 +122,7 @@ def shape_table(kq, torch, np, synth, dev):
             row[name] = {"GBps": round(nbytes / sec / 1e9, 1), "Gelem_s": round(T * d / sec / 1e9, 1),
                          "pct_peak": round(100 * nbytes / sec / 1e9 / HBM_PEAK_GBS, 1), "us": round(sec * 1e6, 2)}
         out[spec.name] = row
+        kq.kq_tune_reset()
         del Xs, outs
         print(f"# {spec.name}: " + ", ".join(f"{k} {v['GBps']}" for k, v in row.items() if isinstance(v, dict)),
               file=sys.stderr, flush=True)
@@ -358,6 +366,9 @@ def main():
         comparison["smoothquant_mxfp4_GBps"] = rate(lambda i: kq.kq_smooth_quantize(Xs[i & 1], md, *outs[i & 1]))
         comparison["plain_mxfp4_GBps"] = rate(lambda i: kq.kq_mx_quantize(Xs[i & 1], *outs[i & 1]))
         comparison["hadamard32_mxfp4_GBps"] = rate(lambda i: kq.kq_hadamard_quantize(Xs[i & 1], *outs[i & 1]))
+        for hb in (64, 128, 256, 512):
+            comparison[f"hadamard{hb}_mxfp4_GBps"] = rate(
+                lambda i, hb=hb: kq.kq_hadamard_quantize_ex(Xs[i & 1], hb, *outs[i & 1]))
         comparison["kroquant_time_over_smoothquant_time"] = round(comparison["smoothquant_mxfp4_GBps"] / gbs, 4)
         comparison["pages_context"] = ("KroQuant quantizer up to 14% faster than the SmoothQuant kernel on an MI350 "
                                        "(Triton); another machine, context only")
