@@ -57,18 +57,31 @@ struct Params15 {
 // K^T operands of one block for this lane: A[h][s] holds the 8 entries
 // K[8q .. 8q+7][out_channel(h, m)] (q = lane >> 4, m = lane & 15) of term s.
 //
-// From the 15 scalars: one lane builds the five factors in fp64 (G1 .. G5)
-// and stages them in LDS, where the exact path also finds them; every lane then
-// reads the factor entries of its output channel and forms its 8 entries as
-// products in factor order, sharing the partial products of the leading
-// factors (the rounding sequence of each entry is that of kq_build_blocks),
-// rounds them to fp32 and splits them into three bf16 terms.
+// From the 15 scalars: lanes 0 .. 4 each build one factor in fp64 (lane k
+// factor G(k+1)) and stage it in LDS, where the exact path also finds the
+// five; every lane then reads the factor entries of its output channel and
+// forms its 8 entries as products in factor order, sharing the partial
+// products of the leading factors (the rounding sequence of each entry is
+// that of kq_build_blocks), rounds them to fp32 and splits them into three
+// bf16 terms, each rounded to nearest-even from the fp32 entry.
 template <int KSRC>
 __device__ __forceinline__ void setup_a(bf16x8 A[2][3], const Params15& pv, const uint16_t* __restrict__ kblk,
                                         int lane, double* __restrict__ g_lds) {
   const int m = lane & 15, q = lane >> 4;
   if constexpr (KSRC == KSRC_PARAMS) {
-    if (lane == 0) store_factors(factors_f64(pv.v), g_lds);
+    if (lane < 5) {
+      // this lane's factor scalars, written into lanes 1 .. 4 from the
+      // wave-uniform set (lane 0 keeps G1's)
+      float f3[3];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        int v = __float_as_int(pv.v[i]);
+#pragma unroll
+        for (int k = 1; k < 5; ++k) asm("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(__float_as_int(pv.v[3 * k + i])), "i"(k));
+        f3[i] = __int_as_float(v);
+      }
+      store_factor(factor_f64(f3), g_lds + 4 * lane);
+    }
     // LDS accesses of one wave complete in issue order; the fence keeps the
     // compiler from moving the reads above the writes of other lanes.
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -86,7 +99,11 @@ __device__ __forceinline__ void setup_a(bf16x8 A[2][3], const Params15& pv, cons
       const double g5[2] = {e(4, 0), e(4, 1)};
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float k = (float)(p4[i >> 1] * g5[i & 1]);
+        float k = (float)(p4[i >> 1] * g5[i & 1]);
+        // an opaque copy: the bf16 rounding below must start from the fp32
+        // entry (the compiler would otherwise round the fp64 product to bf16
+        // directly, through a longer round-to-odd sequence)
+        asm("" : "+v"(k));
         const __bf16 hi = (__bf16)k;
         const float r1 = k - (float)hi;
         const __bf16 mid = (__bf16)r1;
