@@ -49,6 +49,13 @@ static_assert(kPPT * kThreads == kPieces, "tile pieces must split evenly over th
 // Output channel held by MFMA row m of half h.
 __device__ __forceinline__ int out_channel(int h, int m) { return 8 * (m >> 2) + 4 * h + (m & 3); }
 
+// Two fp32 values rounded to bf16 (nearest even), packed (first in the low half).
+__device__ __forceinline__ unsigned bf16_pair(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) float f32x2;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
 // The 15 scalars of one block, (l, a, b) of G1 .. G5.
 struct Params15 {
   float v[15];
@@ -97,21 +104,24 @@ __device__ __forceinline__ void setup_a(bf16x8 A[2][3], const Params15& pv, cons
 #pragma unroll
       for (int u = 0; u < 4; ++u) p4[u] = p3[u >> 1] * e(3, u & 1);
       const double g5[2] = {e(4, 0), e(4, 1)};
+      u32x4 t[3];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float k = (float)(p4[i >> 1] * g5[i & 1]);
-        // an opaque copy: the bf16 rounding below must start from the fp32
-        // entry (the compiler would otherwise round the fp64 product to bf16
-        // directly, through a longer round-to-odd sequence)
-        asm("" : "+v"(k));
-        const __bf16 hi = (__bf16)k;
-        const float r1 = k - (float)hi;
-        const __bf16 mid = (__bf16)r1;
-        const __bf16 lo = (__bf16)(r1 - (float)mid);
-        A[h][0][i] = hi;
-        A[h][1][i] = mid;
-        A[h][2][i] = lo;
+      for (int u = 0; u < 4; ++u) {  // entries 2u, 2u + 1: one packed pair per term
+        float k0 = (float)(p4[u] * g5[0]), k1 = (float)(p4[u] * g5[1]);
+        // opaque copies: the bf16 roundings below must start from the fp32
+        // entries (the compiler would otherwise round the fp64 products to
+        // bf16 directly, through a longer round-to-odd sequence)
+        asm("" : "+v"(k0), "+v"(k1));
+        const unsigned hi = bf16_pair(k0, k1);
+        const float r0 = k0 - __uint_as_float(hi << 16), r1 = k1 - __uint_as_float(hi & 0xFFFF0000u);
+        const unsigned mid = bf16_pair(r0, r1);
+        const unsigned lo = bf16_pair(r0 - __uint_as_float(mid << 16), r1 - __uint_as_float(mid & 0xFFFF0000u));
+        t[0][u] = hi;
+        t[1][u] = mid;
+        t[2][u] = lo;
       }
+#pragma unroll
+      for (int s = 0; s < 3; ++s) A[h][s] = __builtin_bit_cast(bf16x8, t[s]);
     }
   } else {
 #pragma unroll
