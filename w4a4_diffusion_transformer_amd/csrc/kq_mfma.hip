@@ -84,7 +84,10 @@ __device__ __forceinline__ void setup_a(bf16x8 A[2][3], const Params15& pv, cons
       for (int i = 0; i < 3; ++i) {
         int v = __float_as_int(pv.v[i]);
 #pragma unroll
-        for (int k = 1; k < 5; ++k) asm("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(__float_as_int(pv.v[3 * k + i])), "i"(k));
+        for (int k = 1; k < 5; ++k) {
+          const int src = __builtin_amdgcn_readfirstlane(__float_as_int(pv.v[3 * k + i]));  // uniform
+          asm("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(src), "i"(k));
+        }
         f3[i] = __int_as_float(v);
       }
       store_factor(factor_f64(f3), g_lds + 4 * lane);
