@@ -6,20 +6,24 @@
 // that Y approximates X W^T (Pith review, circularity check: Eq. (1); the
 // W4A4 MXFP4 GEMM the quantizer feeds).
 //
-// v_mfma_scale_f32_16x16x128_f8f6f4 with both operands E2M1: lane l holds 32
-// consecutive K values (16 bytes) of row l % 16 at K offset 32 (l / 16) -
-// exactly one MX block - plus that block's E8M0 byte as its scale operand;
-// the result lane l holds D[4 (l / 16) + i][l % 16], i = 0..3 (verified on
-// MI355X against a CPU evaluation).  Products of E2M1 values and power-of-two
-// scales are exact; sums are fp32.
+// v_mfma_scale_f32_32x32x64_f8f6f4 with both operands E2M1: lane l holds 32
+// consecutive K values (16 bytes) of row l % 32 at K offset 32 (l / 32) -
+// one MX block - and takes that block's E8M0 byte from its scale register
+// (its low byte); result register r of lane l
+// is D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32] (verified on MI355X against a
+// CPU evaluation).  Products of E2M1 values and power-of-two scales are
+// exact; sums are fp32.
 //
-// Workgroup: 4 waves (2 x 2), a 128 x 128 tile of Y, each wave 64 x 64
-// (4 x 4 MFMA tiles).  Per K step of 128: the A and B tiles (128 rows x 64 B
-// each) and their scale bytes are staged through double-buffered LDS (row
-// stride 80 B: the 16 rows an MFMA fragment reads fall on distinct banks);
-// the next step's global loads are in flight during the current step's
-// MFMAs; one barrier per step.  Rows past M or N and K blocks past K read as
-// zero codes (buffer range / masked offsets), which contribute nothing.
+// Workgroup: 8 waves (2 along M x 4 along N), a 256 x 256 tile of Y, each
+// wave 128 x 64 (4 x 2 MFMA tiles of 32 x 32).  K advances 128 per stage.
+// The A and B stage tiles (256 rows x 64 B each) and their scale bytes go
+// from global memory straight into LDS (buffer loads with the LDS bit), in a
+// ring of four stages: three are in flight while one is multiplied.  Rows of
+// a staged tile are 64 B; the 16-byte chunk c of row r sits at position
+// c ^ ((r / 4) % 4), so that the 16 rows one fragment read touches at a
+// fixed chunk fall on distinct banks.  Rows past M or N and K blocks past K
+// load as zero codes (buffer range / out-of-range offsets), which add
+// nothing.
 #include "kq_device.hpp"
 #include "kq_internal.h"
 
@@ -28,144 +32,220 @@ namespace kq {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-constexpr int kThreads = 256;
-constexpr int kBM = 128, kBN = 128;  // tile of Y
-constexpr int kStride = 80;          // LDS bytes per staged row (64 B of codes + 16 B pad)
-constexpr int kTileBytes = kBM * kStride;
+constexpr int kThreads = 512;
+constexpr int kBM = 256, kBN = 256;  // tile of Y
+constexpr int kStages = 4;           // LDS ring
+constexpr int kRowB = 64;            // bytes per staged row (128 K values)
+constexpr int kTileB = kBM * kRowB;  // 16 KB per operand per stage
+constexpr int kScB = kBM * 16;       // scale words per operand per stage: [row][K block] (one dword each)
+
+// Loads into LDS issued as asm, so that the compiler inserts no waits of its
+// own for them; the loop waits explicitly (s_waitcnt vmcnt) before the
+// barrier that publishes a stage.  Lane i writes LDS bytes m0 + size * i.
+__device__ __forceinline__ void dma_b128(u32x4 desc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_nop 1\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "{m0}"(lds), "v"(voff), "s"(desc)
+               : "memory");
+}
+__device__ __forceinline__ void dma_b8(u32x4 desc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_nop 1\n\tbuffer_load_ubyte %1, %2, 0 offen lds"
+               :
+               : "{m0}"(lds), "v"(voff), "s"(desc)
+               : "memory");
+}
+
+// An FP4 operand: the instruction reads only the first four registers of
+// the eight-register operand when the format is E2M1, so the rest is left
+// undefined (no moves to fill it).
+__device__ __forceinline__ i32x8 fp4_operand(u32x4 v) {
+  typedef __attribute__((ext_vector_type(4))) int i32x4;
+  const i32x4 w = __builtin_bit_cast(i32x4, v);
+  return __builtin_shufflevector(w, w, 0, 1, 2, 3, -1, -1, -1, -1);
+}
+
+// Raw buffer descriptor words over [base, base + bytes), in scalar registers.
+__device__ __forceinline__ u32x4 desc_uniform(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (bytes >= kMaxRecords ? kMaxRecords : (int)bytes);
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  u32x4 dsc;
+  dsc[0] = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)b);
+  dsc[1] = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(b >> 32)) & 0xFFFFu;
+  dsc[2] = (unsigned)__builtin_amdgcn_readfirstlane(n);
+  dsc[3] = (unsigned)kRsrcFlags;
+  return dsc;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Workgroup barrier with no implied wait (each wave has waited for its own
+// loads into LDS); the empty asm statements keep the compiler from moving
+// LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
 
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t a_lds[2][kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t b_lds[2][kTileBytes];
-  __shared__ uint8_t as_lds[2][kBM * 4];
-  __shared__ uint8_t bs_lds[2][kBN * 4];
+  __shared__ __attribute__((aligned(1024))) uint8_t a_st[kStages][kTileB];
+  __shared__ __attribute__((aligned(1024))) uint8_t b_st[kStages][kTileB];
+  __shared__ __attribute__((aligned(256))) uint8_t as_st[kStages][kScB];
+  __shared__ __attribute__((aligned(256))) uint8_t bs_st[kStages][kScB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wm = wv >> 2, wn = wv & 3;
   const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
   const int K = g.K, kbytes = K >> 1, kblocks = K >> 5;
   const int nsteps = (K + 127) >> 7;
   const int mrows = min(kBM, g.M - m0), nrows = min(kBN, g.N - n0);
 
-  // Per-workgroup descriptors over this tile's rows (reads past them give zero).
-  const auto ra = rsrc_uniform(g.a_codes + (int64_t)m0 * kbytes, (int64_t)mrows * kbytes);
-  const auto rb = rsrc_uniform(g.b_codes + (int64_t)n0 * kbytes, (int64_t)nrows * kbytes);
-  const auto ras = rsrc_uniform(g.a_scales + (int64_t)m0 * kblocks, (int64_t)mrows * kblocks);
-  const auto rbs = rsrc_uniform(g.b_scales + (int64_t)n0 * kblocks, (int64_t)nrows * kblocks);
-
-  // Code pieces this thread moves per step: 2 of A, 2 of B (row p / 4, 16-byte chunk p % 4).
-  int prow[2], pchk[2];
+  // Loads of one stage: this wave moves the 16-row groups 2 wv and 2 wv + 1
+  // of A and of B (codes: lane l -> row l / 4 of the group, LDS position
+  // l % 4, holding chunk (l % 4) ^ ((l / 16) % 4); scales: lane l -> row
+  // l / 4, K block l % 4, a byte load that lands as one zero-extended dword
+  // per lane).  Descriptors cover only the group's rows.
+  u32x4 da[2], db[2], dsa[2], dsb[2];
+  uint32_t crow_off, srow_off;
+  const int cchunk = (lane & 3) ^ ((lane >> 4) & 3), sblk = lane & 3;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    const int p = tid + kThreads * k;
-    prow[k] = p >> 2;
-    pchk[k] = p & 3;
+    const int G = 2 * wv + k;
+    const int ra = min(16, max(0, mrows - 16 * G)), rb = min(16, max(0, nrows - 16 * G));
+    da[k] = desc_uniform(g.a_codes + (int64_t)(m0 + 16 * G) * kbytes, (int64_t)ra * kbytes);
+    db[k] = desc_uniform(g.b_codes + (int64_t)(n0 + 16 * G) * kbytes, (int64_t)rb * kbytes);
+    dsa[k] = desc_uniform(g.a_scales + (int64_t)(m0 + 16 * G) * kblocks, (int64_t)ra * kblocks);
+    dsb[k] = desc_uniform(g.b_scales + (int64_t)(n0 + 16 * G) * kblocks, (int64_t)rb * kblocks);
   }
-  // Scale bytes: threads 0..127 move row tid of A, 128..255 row tid - 128 of B (4 blocks each).
-  const int srow = tid & 127;
-  const bool s_is_a = wv < 2;  // waves 0, 1 (wave-uniform, so the descriptor choice stays scalar)
+  crow_off = (uint32_t)((lane >> 2) * kbytes);
+  srow_off = (uint32_t)((lane >> 2) * kblocks);
 
-  u32x4 ra_reg[2], rb_reg[2];
-  unsigned s_reg;
-  auto gload = [&](int ks) {
+  auto issue = [&](int ks, int slot) {
+    const bool cin = ks * 128 + 32 * cchunk < K, sin = 4 * ks + sblk < kblocks;
+    const uint32_t co = cin ? crow_off + (uint32_t)(64 * ks + 16 * cchunk) : kOut;
+    const uint32_t so = sin ? srow_off + (uint32_t)(4 * ks + sblk) : kOut;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const bool kin = ks * 128 + 32 * pchk[k] < K;
-      const uint32_t off = kin ? (uint32_t)(prow[k] * kbytes + ks * 64 + 16 * pchk[k]) : kOut;
-      ra_reg[k] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
-      rb_reg[k] = __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0);
+      const int G = 2 * wv + k;
+      dma_b128(da[k], co, lds_addr(&a_st[slot][1024 * G]));
+      dma_b128(db[k], co, lds_addr(&b_st[slot][1024 * G]));
+      dma_b8(dsa[k], so, lds_addr(&as_st[slot][256 * G]));
+      dma_b8(dsb[k], so, lds_addr(&bs_st[slot][256 * G]));
     }
-    unsigned v = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const bool kin = 4 * ks + b < kblocks;
-      const uint32_t off = kin ? (uint32_t)(srow * kblocks + 4 * ks + b) : kOut;
-      const unsigned byte = __builtin_amdgcn_raw_buffer_load_b8(s_is_a ? ras : rbs, off, 0, 0);
-      v |= (byte & 0xFFu) << (8 * b);
-    }
-    s_reg = v;
-  };
-  auto lwrite = [&](int buf) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      *reinterpret_cast<u32x4*>(&a_lds[buf][prow[k] * kStride + 16 * pchk[k]]) = ra_reg[k];
-      *reinterpret_cast<u32x4*>(&b_lds[buf][prow[k] * kStride + 16 * pchk[k]]) = rb_reg[k];
-    }
-    *reinterpret_cast<unsigned*>(s_is_a ? &as_lds[buf][srow * 4] : &bs_lds[buf][srow * 4]) = s_reg;
   };
 
-  f32x4 acc[4][4];
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int fr = lane & 15, fg = lane >> 4;  // fragment row within 16, K block within the step
-  auto compute = [&](int buf) {
-    i32x8 af[4], bf[4];
-    int sa[4], sb[4];
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int ar = 64 * wm + 16 * t + fr, br = 64 * wn + 16 * t + fr;
-      const u32x4 va = *reinterpret_cast<const u32x4*>(&a_lds[buf][ar * kStride + 16 * fg]);
-      const u32x4 vb = *reinterpret_cast<const u32x4*>(&b_lds[buf][br * kStride + 16 * fg]);
-      af[t] = i32x8{(int)va[0], (int)va[1], (int)va[2], (int)va[3], 0, 0, 0, 0};
-      bf[t] = i32x8{(int)vb[0], (int)vb[1], (int)vb[2], (int)vb[3], 0, 0, 0, 0};
-      sa[t] = as_lds[buf][ar * 4 + fg];
-      sb[t] = bs_lds[buf][br * 4 + fg];
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // Fragment rows of this lane and its K half within a 64-K sub-step.
+  const int fr = lane & 31, fh = lane >> 5;
+  auto compute = [&](int slot) {
+    const uint8_t* as = a_st[slot];
+    const uint8_t* bs = b_st[slot];
+    // scale words of K blocks fh (sub-step 0) and 2 + fh (sub-step 1) of this lane's rows
+    int sa[2][4], sb[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int R = 128 * wm + 32 * i + fr;
+        sa[s][i] = *reinterpret_cast<const int*>(&as_st[slot][16 * R + 4 * (2 * s + fh)]);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int R = 64 * wn + 32 * j + fr;
+        sb[s][j] = *reinterpret_cast<const int*>(&bs_st[slot][16 * R + 4 * (2 * s + fh)]);
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int s = 0; s < 2; ++s) {
+      const int c = 2 * s + fh;
+      i32x8 af[4], bf[2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf[j], acc[i][j], 4, 4, 0, sa[i], 0,
-                                                                      sb[j]);
+      for (int i = 0; i < 4; ++i) {
+        const int R = 128 * wm + 32 * i + fr;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&as[64 * R + 16 * (c ^ ((R >> 2) & 3))]);
+        af[i] = fp4_operand(v);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int R = 64 * wn + 32 * j + fr;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&bs[64 * R + 16 * (c ^ ((R >> 2) & 3))]);
+        bf[j] = fp4_operand(v);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 4, 4, 0, sa[s][i], 0,
+                                                                      sb[s][j]);
+    }
   };
 
-  gload(0);
-  lwrite(0);
-  __syncthreads();
+  // Stages 0 .. 2 in flight; per stage ks: wait until this wave's loads of
+  // stage ks have landed (the loads of stages ks + 1 and ks + 2, 16
+  // operations, may stay outstanding), barrier, load stage ks + 3 into the
+  // slot stage ks - 1 used (every wave is past it), multiply stage ks.
+  // Stages past the end load nothing but zeros.
+  issue(0, 0);
+  issue(1, 1);
+  issue(2, 2);
   for (int ks = 0; ks < nsteps; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < nsteps) gload(ks + 1);  // workgroup-uniform
-    compute(buf);
-    if (ks + 1 < nsteps) lwrite(buf ^ 1);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt((16 & 15) | ((16 >> 4) << 14) | 0x70 | 0xF00);  // vmcnt(16)
+    lds_barrier();
+    issue(ks + 3, (ks + 3) & 3);
+    compute(ks & 3);
   }
+  // no load into LDS may still be in flight when the workgroup ends
+  __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);
 
-  // Y rows m0 + 64 wm + 16 i + 4 fg + r, columns n0 + 64 wn + 16 j + fr.
+  // Y rows m0 + 128 wm + 32 i + 8 (r / 4) + 4 fh + r % 4, columns n0 + 64 wn + 32 j + fr; one
+  // descriptor per 32-row band (ranges stay far below 2^31 bytes for any N).
   const int64_t N = g.N;
-  if (g.y_f32) {
-    const auto ry = rsrc_uniform(g.y_f32 + (int64_t)m0 * N, (int64_t)mrows * N * 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int band = 128 * wm + 32 * i;
+    const int brows = min(32, max(0, mrows - band));
+    const int64_t base = (int64_t)(m0 + band) * N;
+    if (g.y_f32) {
+      const auto ry = rsrc_uniform(g.y_f32 + base, (int64_t)brows * N * 4);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = 64 * wn + 16 * j + fr;
+      for (int j = 0; j < 2; ++j) {
+        const int col = 64 * wn + 32 * j + fr;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 64 * wm + 16 * i + 4 * fg + r;
+        for (int r = 0; r < 16; ++r) {
+          const int row = 8 * (r >> 2) + 4 * fh + (r & 3);
           const uint32_t off = col < nrows ? (uint32_t)((row * N + n0 + col) * 4) : kOut;
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), ry, off, 0, 0);
         }
       }
-  }
-  if (g.y_bf16) {
-    const auto ry = rsrc_uniform(g.y_bf16 + (int64_t)m0 * N, (int64_t)mrows * N * 2);
+    }
+    if (g.y_bf16) {
+      const auto ry = rsrc_uniform(g.y_bf16 + base, (int64_t)brows * N * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 2; ++j) {
+        const int col = 64 * wn + 32 * j + fr;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = 64 * wn + 16 * j + fr;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 64 * wm + 16 * i + 4 * fg + r;
+        for (int r = 0; r < 16; ++r) {
+          const int row = 8 * (r >> 2) + 4 * fh + (r & 3);
           const uint32_t off = col < nrows ? (uint32_t)((row * N + n0 + col) * 2) : kOut;
           const __bf16 h = (__bf16)acc[i][j][r];
           __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, h), ry, off, 0, 0);
         }
       }
+    }
   }
 }
 
