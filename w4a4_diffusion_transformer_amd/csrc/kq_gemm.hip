@@ -27,6 +27,9 @@
 #include "kq_device.hpp"
 #include "kq_internal.h"
 
+#ifndef GROUPM
+#define GROUPM 4
+#endif
 namespace kq {
 
 namespace {
@@ -39,6 +42,7 @@ constexpr int kBM = 256, kBN = 256;  // tile of Y
 constexpr int kStages = 4;           // LDS ring
 constexpr int kRowB = 64;            // bytes per staged row (128 K values)
 constexpr int kTileB = kBM * kRowB;  // 16 KB per operand per stage
+constexpr int kGroupM = GROUPM;      // M tiles per group of the tile order
 constexpr int kScB = kBM * 16;       // scale words per operand per stage: [row][K block] (one dword each)
 
 // Loads into LDS issued as asm, so that the compiler inserts no waits of its
@@ -102,7 +106,22 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv >> 2, wn = wv & 3;
-  const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
+  // Tile of this workgroup: the tiles are numbered in groups of kGroupM M
+  // tiles, column by column; XCD x (workgroups are dealt to the eight XCDs
+  // in turn) takes the x-th eighth of that order, so the workgroups running
+  // at once on one XCD share A rows and B rows in its L2.
+  int tm, tn;
+  {
+    const int gm = (g.M + kBM - 1) / kBM, gn = (g.N + kBN - 1) / kBN;
+    const int t = xcd_remap((int)blockIdx.x, gm * gn);
+    const int per_group = kGroupM * gn;
+    const int grp = t / per_group, first = grp * kGroupM;
+    const int rows = min(kGroupM, gm - first);
+    const int w = t - grp * per_group;
+    tm = first + w % rows;
+    tn = w / rows;
+  }
+  const int m0 = tm * kBM, n0 = tn * kBN;
   const int K = g.K, kbytes = K >> 1, kblocks = K >> 5;
   const int nsteps = (K + 127) >> 7;
   const int mrows = min(kBM, g.M - m0), nrows = min(kBN, g.N - n0);
@@ -154,20 +173,23 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   auto compute = [&](int slot) {
     const uint8_t* as = a_st[slot];
     const uint8_t* bs = b_st[slot];
-    // scale words of K blocks fh (sub-step 0) and 2 + fh (sub-step 1) of this lane's rows
+    // scale words of K blocks fh (sub-step 0) and 2 + fh (sub-step 1) of this
+    // lane's rows: the row's four words in one 16-byte read (consecutive
+    // lanes, consecutive 16 bytes: no bank conflicts), then picked per lane half
     int sa[2][4], sb[2][2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int i = 0; i < 4; ++i) {
+      const int R = 128 * wm + 32 * i + fr;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(&as_st[slot][16 * R]);
+      sa[0][i] = (int)(fh ? w[1] : w[0]);
+      sa[1][i] = (int)(fh ? w[3] : w[2]);
+    }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int R = 128 * wm + 32 * i + fr;
-        sa[s][i] = *reinterpret_cast<const int*>(&as_st[slot][16 * R + 4 * (2 * s + fh)]);
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int R = 64 * wn + 32 * j + fr;
-        sb[s][j] = *reinterpret_cast<const int*>(&bs_st[slot][16 * R + 4 * (2 * s + fh)]);
-      }
+    for (int j = 0; j < 2; ++j) {
+      const int R = 64 * wn + 32 * j + fr;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(&bs_st[slot][16 * R]);
+      sb[0][j] = (int)(fh ? w[1] : w[0]);
+      sb[1][j] = (int)(fh ? w[3] : w[2]);
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -253,7 +275,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 
 hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
   GemmArgs g = args;
-  const dim3 grid((unsigned)((g.N + kBN - 1) / kBN), (unsigned)((g.M + kBM - 1) / kBM));
+  const dim3 grid((unsigned)(((g.N + kBN - 1) / kBN) * ((g.M + kBM - 1) / kBM)));
   void* kargs[] = {&g};
   return hipLaunchKernel((const void*)&gemm_kernel, grid, dim3(kThreads), kargs, 0, stream);
 }
