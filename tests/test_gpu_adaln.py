@@ -112,7 +112,8 @@ def check(name, X, P, st, sc, sh, tps, variant, against_unfused=True):
 # ---------------------------------------------------------------- row statistics
 
 
-@pytest.mark.parametrize("T,d", [(1, 32), (7, 64), (33, 1152), (300, 3072), (64, 12288), (1000, 160)])
+@pytest.mark.parametrize("T,d", [(1, 32), (7, 64), (33, 1152), (300, 3072), (64, 12288), (1000, 160), (5, 16416),
+                                 (37, 4608), (19, 8224)])
 def test_row_stats(T, d):
     X = synth.random_matrix(T, d, seed=T + d, n_outliers=max(1, d // 64), mult=80.0)
     st = torch.empty((T, 2), dtype=torch.float32, device="cuda:0")

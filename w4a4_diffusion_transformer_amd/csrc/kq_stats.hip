@@ -11,8 +11,13 @@
 // the fp32 results agree with a sequential evaluation except, rarely, by one
 // ulp.
 //
-// One workgroup per row (grid-strided): two passes over the row, the second
-// served mostly from L2, block reductions through LDS.
+// Rows up to 4096 channels: one wave per row, no LDS and no barriers; lane
+// l holds the row's 16-byte pieces l, l + 64, ... in registers, so the row
+// is read from HBM once, and both sums are reduced with wave shuffles.  Rows
+// up to 16384 channels: one four-wave workgroup per row, the row again held
+// in registers, the sums reduced across the waves through LDS.  Longer rows:
+// the same workgroup shape in two passes over memory.  Rows are grid-strided
+// over a launch sized to fill the GPU once.
 #include "kq_device.hpp"
 #include "kq_internal.h"
 
@@ -20,48 +25,91 @@ namespace kq {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
 
-__device__ __forceinline__ double block_sum(double v, double* red) {
+__device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();  // red[] may still be read from the previous reduction
-  if ((threadIdx.x & 63) == 0) red[w] = v;
-  __syncthreads();
+  return v;
+}
+
+__device__ __forceinline__ double piece_sum(u32x4 v) {
+#pragma clang fp contract(off)
   double s = 0.0;
 #pragma unroll
-  for (int i = 0; i < kThreads / 64; ++i) s += red[i];
+  for (int k = 0; k < 4; ++k) s += (double)bf16_lo(v[k]) + (double)bf16_hi(v[k]);
   return s;
 }
 
+__device__ __forceinline__ double piece_sq(u32x4 v, double mean) {
+#pragma clang fp contract(off)
+  double q = 0.0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const double u0 = (double)bf16_lo(v[k]) - mean;
+    const double u1 = (double)bf16_hi(v[k]) - mean;
+    q += u0 * u0;
+    q += u1 * u1;
+  }
+  return q;
+}
+
+// Sum over the WPR waves of one row (WPR > 1: the whole workgroup is one row).
+template <int WPR>
+__device__ __forceinline__ double row_sum(double v, double* red) {
+  v = wave_sum(v);
+  if constexpr (WPR > 1) {
+    const int w = threadIdx.x >> 6;
+    __syncthreads();  // red[] may still be read from the previous reduction
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    v = 0.0;
+#pragma unroll
+    for (int i = 0; i < WPR; ++i) v += red[i];
+  }
+  return v;
+}
+
+// WPR waves per row (1: each wave its own row; kWaves: the workgroup), MAXP
+// register-resident 16-byte pieces per thread (0: two passes over memory).
+template <int WPR, int MAXP>
 __global__ __launch_bounds__(kThreads) void row_stats_kernel(const uint16_t* __restrict__ X, int T, int d,
                                                              double eps, float* __restrict__ stats) {
 #pragma clang fp contract(off)
-  __shared__ double red[kThreads / 64];
+  __shared__ double red[kWaves];
+  constexpr int kRowThreads = 64 * WPR, kRowsPerStep = kWaves / WPR;
+  const int t = threadIdx.x % kRowThreads;
+  const int slot = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kRowThreads));
   const int npieces = d >> 3;  // 8 bf16 per 16-byte piece
-  for (int row = blockIdx.x; row < T; row += gridDim.x) {
-    const u32x4* x = reinterpret_cast<const u32x4*>(X + (int64_t)row * d);
-    double s = 0.0;
-    for (int p = threadIdx.x; p < npieces; p += kThreads) {
-      const u32x4 v = x[p];
+  const int step = gridDim.x * kRowsPerStep;
+  for (int row = blockIdx.x * kRowsPerStep + slot; row < T; row += step) {
+    const auto rx = rsrc_uniform(X + (int64_t)row * d, (int64_t)d * 2);  // pieces past the row read as zero
+    double s = 0.0, qs = 0.0, mean;
+    if constexpr (MAXP > 0) {
+      u32x4 v[MAXP];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) s += (double)bf16_lo(v[k]) + (double)bf16_hi(v[k]);
-    }
-    const double mean = block_sum(s, red) / (double)d;
-    double qs = 0.0;
-    for (int p = threadIdx.x; p < npieces; p += kThreads) {
-      const u32x4 v = x[p];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const double u0 = (double)bf16_lo(v[k]) - mean;
-        const double u1 = (double)bf16_hi(v[k]) - mean;
-        qs += u0 * u0;
-        qs += u1 * u1;
+      for (int k = 0; k < MAXP; ++k) {
+        const int p = t + kRowThreads * k;
+        v[k] = __builtin_amdgcn_raw_buffer_load_b128(rx, p < npieces ? (uint32_t)(16 * p) : kOut, 0, kNT);
       }
+#pragma unroll
+      for (int k = 0; k < MAXP; ++k) s += piece_sum(v[k]);
+      mean = row_sum<WPR>(s, red) / (double)d;
+#pragma unroll
+      for (int k = 0; k < MAXP; ++k)
+        if (t + kRowThreads * k < npieces) qs += piece_sq(v[k], mean);
+    } else {
+#pragma unroll 4
+      for (int p = t; p < npieces; p += kRowThreads)
+        s += piece_sum(__builtin_amdgcn_raw_buffer_load_b128(rx, 16 * p, 0, 0));
+      mean = row_sum<WPR>(s, red) / (double)d;
+#pragma unroll 4
+      for (int p = t; p < npieces; p += kRowThreads)
+        qs += piece_sq(__builtin_amdgcn_raw_buffer_load_b128(rx, 16 * p, 0, 0), mean);
     }
-    const double var = block_sum(qs, red) / (double)d;
-    if (threadIdx.x == 0) {
+    const double var = row_sum<WPR>(qs, red) / (double)d;
+    if (t == 0) {
       stats[2 * (int64_t)row] = (float)mean;
       stats[2 * (int64_t)row + 1] = (float)(1.0 / sqrt(var + eps));
     }
@@ -71,9 +119,28 @@ __global__ __launch_bounds__(kThreads) void row_stats_kernel(const uint16_t* __r
 }  // namespace
 
 hipError_t launch_row_stats(const uint16_t* X, int T, int d, double eps, float* stats, hipStream_t stream) {
-  const int grid = T < 4096 ? T : 4096;
+  const int pieces = d / 8;  // 16-byte pieces per row
+  const void* fn;
+  int rows_per_wg;
+  if (pieces <= 64 * 4) {
+    fn = (const void*)&row_stats_kernel<1, 4>;
+    rows_per_wg = kWaves;
+  } else if (pieces <= 64 * 8) {
+    fn = (const void*)&row_stats_kernel<1, 8>;
+    rows_per_wg = kWaves;
+  } else if (pieces <= kThreads * 8) {
+    fn = (const void*)&row_stats_kernel<kWaves, 8>;
+    rows_per_wg = 1;
+  } else {
+    fn = (const void*)&row_stats_kernel<kWaves, 0>;
+    rows_per_wg = 1;
+  }
+  const int64_t slots = (int64_t)cu_count() * resident_per_cu(fn, kThreads);
+  const int64_t need = ((int64_t)T + rows_per_wg - 1) / rows_per_wg;
+  const int grid = (int)(need < slots ? need : slots);
+  if (grid == 0) return hipSuccess;
   void* kargs[] = {&X, &T, &d, &eps, &stats};
-  return hipLaunchKernel((const void*)&row_stats_kernel, dim3(grid), dim3(kThreads), kargs, 0, stream);
+  return hipLaunchKernel(fn, dim3(grid), dim3(kThreads), kargs, 0, stream);
 }
 
 }  // namespace kq
