@@ -326,6 +326,21 @@ def test_guard_bands_and_determinism():
         np.testing.assert_array_equal(outs[i][1], outs[i + 1][1])
 
 
+@pytest.mark.parametrize("shape", [(96, 1152), (257, 3072), (64, 12288)])
+def test_otf_split_equals_prebuilt_split(shape):
+    """The in-kernel K setup rounds each fp32 entry to its bf16 terms exactly as kq_build_blocks does, so
+    the two MFMA variants feed the same operands and agree bit for bit (transformed values, codes, scales)."""
+    T, d = shape
+    nb = d // 32
+    X = synth.random_matrix(T, d, seed=T + 7, n_outliers=nb // 4, mult=60.0)
+    P = synth.random_params(nb, seed=d + 3, sigma_lb=0.4, sigma_a=0.4)
+    c_otf, s_otf, y_otf = run_kron(X, P, "mfma_otf", want_y=True)
+    c_den, s_den, y_den = run_kron(X, P, "mfma_dense", want_y=True)
+    np.testing.assert_array_equal(y_otf.view(np.uint32), y_den.view(np.uint32))
+    np.testing.assert_array_equal(s_otf, s_den)
+    np.testing.assert_array_equal(c_otf, c_den)
+
+
 def test_zero_tokens_is_noop():
     Xd = torch.zeros((0, 64), dtype=torch.int16, device="cuda:0")
     codes = torch.full((16,), 7, dtype=torch.uint8, device="cuda:0")
