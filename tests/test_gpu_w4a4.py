@@ -118,7 +118,7 @@ def run_gemm(a_codes, a_scales, b_codes, b_scales):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 1, 32), (128, 128, 128), (77, 200, 160), (300, 257, 2240), (512, 384, 1152),
-                                   (16, 640, 5600), (256, 130, 12288)])
+                                   (16, 640, 5600), (256, 130, 12288), (33, 45, 96), (260, 300, 1504)])
 def test_gemm_parity(M, N, K):
     ac, as_ = random_mx(M, K, seed=M * 3 + K)
     bc, bs = random_mx(N, K, seed=N * 5 + K + 1)

@@ -16,12 +16,13 @@
 //
 // Workgroup: 8 waves (2 along M x 4 along N), a 256 x 256 tile of Y, each
 // wave 128 x 64 (4 x 2 MFMA tiles of 32 x 32).  K advances 128 per stage.
-// The A and B stage tiles (256 rows x 64 B each) and their scale bytes go
-// from global memory straight into LDS (buffer loads with the LDS bit), in a
-// ring of four stages: three are in flight while one is multiplied.  Rows of
-// a staged tile are 64 B; the 16-byte chunk c of row r sits at position
-// c ^ ((r / 4) % 4), so that the 16 rows one fragment read touches at a
-// fixed chunk fall on distinct banks.  Rows past M or N and K blocks past K
+// The A and B stage tiles (256 rows x 64 B each) go from global memory
+// straight into LDS (buffer loads with the LDS bit), in a ring of four
+// stages: three are in flight while one is multiplied.  Scale bytes go the
+// same way, 16 K blocks (four stages) of a row per 16-byte load, into a ring
+// of two such groups.  Rows of a staged tile are 64 B; the 16-byte chunk c
+// of row r sits at position c ^ ((r / 4) % 4), so that the 16 rows one
+// fragment read touches at a fixed chunk fall on distinct banks.  Rows past M or N and K blocks past K
 // load as zero codes (buffer range / out-of-range offsets), which add
 // nothing.
 #include "kq_device.hpp"
@@ -43,7 +44,7 @@ constexpr int kStages = 4;           // LDS ring
 constexpr int kRowB = 64;            // bytes per staged row (128 K values)
 constexpr int kTileB = kBM * kRowB;  // 16 KB per operand per stage
 constexpr int kGroupM = GROUPM;      // M tiles per group of the tile order
-constexpr int kScB = kBM * 16;       // scale words per operand per stage: [row][K block] (one dword each)
+constexpr int kScB = kBM * 16;       // scale bytes per operand per group of 4 stages: [row][16 K blocks]
 
 // Loads into LDS issued as asm, so that the compiler inserts no waits of its
 // own for them; the loop waits explicitly (s_waitcnt vmcnt) before the
@@ -54,13 +55,6 @@ __device__ __forceinline__ void dma_b128(u32x4 desc, uint32_t voff, uint32_t lds
                : "{m0}"(lds), "v"(voff), "s"(desc)
                : "memory");
 }
-__device__ __forceinline__ void dma_b8(u32x4 desc, uint32_t voff, uint32_t lds) {
-  asm volatile("s_nop 1\n\tbuffer_load_ubyte %1, %2, 0 offen lds"
-               :
-               : "{m0}"(lds), "v"(voff), "s"(desc)
-               : "memory");
-}
-
 // An FP4 operand: the instruction reads only the first four registers of
 // the eight-register operand when the format is E2M1, so the rest is left
 // undefined (no moves to fill it).
@@ -100,8 +94,8 @@ __device__ __forceinline__ void lds_barrier() {
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(1024))) uint8_t a_st[kStages][kTileB];
   __shared__ __attribute__((aligned(1024))) uint8_t b_st[kStages][kTileB];
-  __shared__ __attribute__((aligned(256))) uint8_t as_st[kStages][kScB];
-  __shared__ __attribute__((aligned(256))) uint8_t bs_st[kStages][kScB];
+  __shared__ __attribute__((aligned(256))) uint8_t as_st[2][kScB];  // by parity of the stage group
+  __shared__ __attribute__((aligned(256))) uint8_t bs_st[2][kScB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -126,37 +120,65 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   const int nsteps = (K + 127) >> 7;
   const int mrows = min(kBM, g.M - m0), nrows = min(kBN, g.N - n0);
 
-  // Loads of one stage: this wave moves the 16-row groups 2 wv and 2 wv + 1
-  // of A and of B (codes: lane l -> row l / 4 of the group, LDS position
-  // l % 4, holding chunk (l % 4) ^ ((l / 16) % 4); scales: lane l -> row
-  // l / 4, K block l % 4, a byte load that lands as one zero-extended dword
-  // per lane).  Descriptors cover only the group's rows.
-  u32x4 da[2], db[2], dsa[2], dsb[2];
-  uint32_t crow_off, srow_off;
-  const int cchunk = (lane & 3) ^ ((lane >> 4) & 3), sblk = lane & 3;
+  // Code loads of one stage: this wave moves the 16-row groups 2 wv and
+  // 2 wv + 1 of A and of B (lane l -> row l / 4 of the group, LDS position
+  // l % 4, holding chunk (l % 4) ^ ((l / 16) % 4)).  Scale loads, once per
+  // group of 4 stages: wave w < 4 moves the 16 scale bytes (K blocks of the
+  // 4 stages) of A rows 64 w .. 64 w + 63, wave w >= 4 those of B rows
+  // 64 (w - 4) ..; one 16-byte load per lane and row (byte offsets need no
+  // alignment for these loads: checked on MI355X).  The code descriptors
+  // cover only the rows a load may touch; the scale descriptors run to the
+  // end of the scale tensor, since a row's last 16-byte piece reaches into
+  // the next row.  A dword that crosses the end of a range reads as zero
+  // (range checks are per dword: checked on MI355X), so when K / 32 is not a
+  // multiple of 4 the final (K / 32) % 4 scale bytes of the last row of A
+  // and of B are read here with ordinary loads and patched in at the last
+  // stage.
+  u32x4 da[2], db[2], dsc;
+  const int cchunk = (lane & 3) ^ ((lane >> 4) & 3);
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int G = 2 * wv + k;
     const int ra = min(16, max(0, mrows - 16 * G)), rb = min(16, max(0, nrows - 16 * G));
     da[k] = desc_uniform(g.a_codes + (int64_t)(m0 + 16 * G) * kbytes, (int64_t)ra * kbytes);
     db[k] = desc_uniform(g.b_codes + (int64_t)(n0 + 16 * G) * kbytes, (int64_t)rb * kbytes);
-    dsa[k] = desc_uniform(g.a_scales + (int64_t)(m0 + 16 * G) * kblocks, (int64_t)ra * kblocks);
-    dsb[k] = desc_uniform(g.b_scales + (int64_t)(n0 + 16 * G) * kblocks, (int64_t)rb * kblocks);
   }
-  crow_off = (uint32_t)((lane >> 2) * kbytes);
-  srow_off = (uint32_t)((lane >> 2) * kblocks);
+  {
+    const bool sa_side = wv < 4;  // wave-uniform
+    const int r0 = 64 * (wv & 3);
+    const int rs = max(0, (sa_side ? g.M - m0 : g.N - n0) - r0);  // rows to the end of the tensor
+    dsc = sa_side ? desc_uniform(g.a_scales + (int64_t)(m0 + r0) * kblocks, (int64_t)rs * kblocks)
+                  : desc_uniform(g.b_scales + (int64_t)(n0 + r0) * kblocks, (int64_t)rs * kblocks);
+  }
+  const int kfull = kblocks & ~3, kr = kblocks & 3;
+  unsigned pa = 0, pb = 0;  // final partial scale dwords of rows M - 1 and N - 1
+  if (kr != 0 && m0 + kBM >= g.M) {
+    const uint8_t* p = g.a_scales + (int64_t)(g.M - 1) * kblocks + kfull;
+    for (int j = 0; j < kr; ++j) pa |= (unsigned)p[j] << (8 * j);
+  }
+  if (kr != 0 && n0 + kBN >= g.N) {
+    const uint8_t* p = g.b_scales + (int64_t)(g.N - 1) * kblocks + kfull;
+    for (int j = 0; j < kr; ++j) pb |= (unsigned)p[j] << (8 * j);
+  }
+  const uint32_t crow_off = (uint32_t)((lane >> 2) * kbytes);
+  const uint32_t srow_off = (uint32_t)(lane * kblocks);
 
+  // Vector memory operations this wave issues for stage ks: 4 code loads,
+  // plus the scale load of the stage group when ks opens one.
   auto issue = [&](int ks, int slot) {
-    const bool cin = ks * 128 + 32 * cchunk < K, sin = 4 * ks + sblk < kblocks;
+    const bool cin = ks * 128 + 32 * cchunk < K;
     const uint32_t co = cin ? crow_off + (uint32_t)(64 * ks + 16 * cchunk) : kOut;
-    const uint32_t so = sin ? srow_off + (uint32_t)(4 * ks + sblk) : kOut;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
       const int G = 2 * wv + k;
       dma_b128(da[k], co, lds_addr(&a_st[slot][1024 * G]));
       dma_b128(db[k], co, lds_addr(&b_st[slot][1024 * G]));
-      dma_b8(dsa[k], so, lds_addr(&as_st[slot][256 * G]));
-      dma_b8(dsb[k], so, lds_addr(&bs_st[slot][256 * G]));
+    }
+    if ((ks & 3) == 0) {  // uniform
+      const int p = ks >> 2;
+      const uint32_t so = 16 * p < kblocks ? srow_off + (uint32_t)(16 * p) : kOut;
+      uint8_t* dst = wv < 4 ? &as_st[p & 1][16 * 64 * (wv & 3)] : &bs_st[p & 1][16 * 64 * (wv & 3)];
+      dma_b128(dsc, so, lds_addr(dst));
     }
   };
 
@@ -170,26 +192,34 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 
   // Fragment rows of this lane and its K half within a 64-K sub-step.
   const int fr = lane & 31, fh = lane >> 5;
-  auto compute = [&](int slot) {
+  auto compute = [&](int ks, int slot) {
     const uint8_t* as = a_st[slot];
     const uint8_t* bs = b_st[slot];
-    // scale words of K blocks fh (sub-step 0) and 2 + fh (sub-step 1) of this
-    // lane's rows: the row's four words in one 16-byte read (consecutive
-    // lanes, consecutive 16 bytes: no bank conflicts), then picked per lane half
-    int sa[2][4], sb[2][2];
+    // scale bytes of K blocks 4 ks + fh (sub-step 0: byte 0 after the shift)
+    // and 4 ks + 2 + fh (sub-step 1: byte 2, picked with op_sel); blocks past
+    // K (whose codes load as zero) get the neutral byte 127; only the last
+    // stage can be a tail stage, and only when K / 32 is not a multiple of 4
+    const int grp = (ks >> 2) & 1, wsel = 4 * (ks & 3);
+    const bool tail = 4 * ks + 4 > kblocks;  // uniform
+    auto fix = [&](unsigned w, bool last_row, unsigned patch) {
+      if (tail && last_row) w = patch;
+      w >>= 8 * fh;
+      if (tail) {
+        if (4 * ks + fh >= kblocks) w = (w & ~0xFFu) | 127u;
+        if (4 * ks + 2 + fh >= kblocks) w = (w & ~0xFF0000u) | (127u << 16);
+      }
+      return (int)w;
+    };
+    int sa[4], sb[2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int R = 128 * wm + 32 * i + fr;
-      const u32x4 w = *reinterpret_cast<const u32x4*>(&as_st[slot][16 * R]);
-      sa[0][i] = (int)(fh ? w[1] : w[0]);
-      sa[1][i] = (int)(fh ? w[3] : w[2]);
+      sa[i] = fix(*reinterpret_cast<const unsigned*>(&as_st[grp][16 * R + wsel]), m0 + R == g.M - 1, pa);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int R = 64 * wn + 32 * j + fr;
-      const u32x4 w = *reinterpret_cast<const u32x4*>(&bs_st[slot][16 * R]);
-      sb[0][j] = (int)(fh ? w[1] : w[0]);
-      sb[1][j] = (int)(fh ? w[3] : w[2]);
+      sb[j] = fix(*reinterpret_cast<const unsigned*>(&bs_st[grp][16 * R + wsel]), n0 + R == g.N - 1, pb);
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -210,9 +240,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 4, 4, 0, sa[s][i], 0,
-                                                                      sb[s][j]);
+        for (int j = 0; j < 2; ++j) {
+          if (s == 0)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 4, 4, 0, sa[i], 0,
+                                                                        sb[j]);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 4, 4, 2, sa[i], 2,
+                                                                        sb[j]);
+        }
     }
   };
 
@@ -225,10 +260,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   issue(1, 1);
   issue(2, 2);
   for (int ks = 0; ks < nsteps; ++ks) {
-    __builtin_amdgcn_s_waitcnt((16 & 15) | ((16 >> 4) << 14) | 0x70 | 0xF00);  // vmcnt(16)
+    // loads issued after stage ks's: stages ks + 1 and ks + 2 (8 code loads),
+    // plus one scale load for each of them that opens a stage group
+    if (((ks + 1) & 3) == 0 || ((ks + 2) & 3) == 0)  // uniform
+      __builtin_amdgcn_s_waitcnt((9 & 15) | ((9 >> 4) << 14) | 0x70 | 0xF00);  // vmcnt(9)
+    else
+      __builtin_amdgcn_s_waitcnt((8 & 15) | ((8 >> 4) << 14) | 0x70 | 0xF00);  // vmcnt(8)
     lds_barrier();
     issue(ks + 3, (ks + 3) & 3);
-    compute(ks & 3);
+    compute(ks, ks & 3);
   }
   // no load into LDS may still be in flight when the workgroup ends
   __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);
