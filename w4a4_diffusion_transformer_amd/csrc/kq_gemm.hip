@@ -210,45 +210,48 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
       }
       return (int)w;
     };
-    int sa[4], sb[2];
+    // Every LDS read of the stage is issued before the first MFMA, each into
+    // registers of its own, so the reads overlap one another and the MFMAs
+    // wait only for the operands they take.
+    unsigned wa[4], wb[2];
+    u32x4 va[2][4], vb[2][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int R = 128 * wm + 32 * i + fr;
-      sa[i] = fix(*reinterpret_cast<const unsigned*>(&as_st[grp][16 * R + wsel]), m0 + R == g.M - 1, pa);
-    }
+    for (int i = 0; i < 4; ++i) wa[i] = *reinterpret_cast<const unsigned*>(&as_st[grp][16 * (128 * wm + 32 * i + fr) + wsel]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int R = 64 * wn + 32 * j + fr;
-      sb[j] = fix(*reinterpret_cast<const unsigned*>(&bs_st[grp][16 * R + wsel]), n0 + R == g.N - 1, pb);
-    }
+    for (int j = 0; j < 2; ++j) wb[j] = *reinterpret_cast<const unsigned*>(&bs_st[grp][16 * (64 * wn + 32 * j + fr) + wsel]);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int c = 2 * s + fh;
-      i32x8 af[4], bf[2];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int R = 128 * wm + 32 * i + fr;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(&as[64 * R + 16 * (c ^ ((R >> 2) & 3))]);
-        af[i] = fp4_operand(v);
+        va[s][i] = *reinterpret_cast<const u32x4*>(&as[64 * R + 16 * (c ^ ((R >> 2) & 3))]);
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int R = 64 * wn + 32 * j + fr;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(&bs[64 * R + 16 * (c ^ ((R >> 2) & 3))]);
-        bf[j] = fp4_operand(v);
+        vb[s][j] = *reinterpret_cast<const u32x4*>(&bs[64 * R + 16 * (c ^ ((R >> 2) & 3))]);
       }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    int sa[4], sb[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sa[i] = fix(wa[i], m0 + 128 * wm + 32 * i + fr == g.M - 1, pa);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) sb[j] = fix(wb[j], n0 + 64 * wn + 32 * j + fr == g.N - 1, pb);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           if (s == 0)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 4, 4, 0, sa[i], 0,
-                                                                        sb[j]);
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4_operand(va[0][i]), fp4_operand(vb[0][j]),
+                                                                        acc[i][j], 4, 4, 0, sa[i], 0, sb[j]);
           else
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 4, 4, 2, sa[i], 2,
-                                                                        sb[j]);
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fp4_operand(va[1][i]), fp4_operand(vb[1][j]),
+                                                                        acc[i][j], 4, 4, 2, sa[i], 2, sb[j]);
         }
-    }
   };
 
   // Stages 0 .. 2 in flight; per stage ks: wait until this wave's loads of
