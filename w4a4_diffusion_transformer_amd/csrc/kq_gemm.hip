@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 
   // Vector memory operations this wave issues for stage ks: 4 code loads,
   // plus the scale load of the stage group when ks opens one.
-  auto issue = [&](int ks, int slot) {
+  auto issue = [&](int ks, int slot, bool opens_group) {
     const bool cin = ks * 128 + 32 * cchunk < K;
     const uint32_t co = cin ? crow_off + (uint32_t)(64 * ks + 16 * cchunk) : kOut;
 #pragma unroll
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
       dma_b128(da[k], co, lds_addr(&a_st[slot][1024 * G]));
       dma_b128(db[k], co, lds_addr(&b_st[slot][1024 * G]));
     }
-    if ((ks & 3) == 0) {  // uniform
+    if (opens_group) {  // ks % 4 == 0
       const int p = ks >> 2;
       const uint32_t so = 16 * p < kblocks ? srow_off + (uint32_t)(16 * p) : kOut;
       uint8_t* dst = wv < 4 ? &as_st[p & 1][16 * 64 * (wv & 3)] : &bs_st[p & 1][16 * 64 * (wv & 3)];
@@ -192,14 +192,21 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
 
   // Fragment rows of this lane and its K half within a 64-K sub-step.
   const int fr = lane & 31, fh = lane >> 5;
-  auto compute = [&](int ks, int slot) {
-    const uint8_t* as = a_st[slot];
-    const uint8_t* bs = b_st[slot];
+  // Scale rows of the current stage group (16 bytes: 4 per stage) of this
+  // lane's A rows 128 wm + 32 i + fr and B rows 64 wn + 32 j + fr, read once
+  // per group as whole rows (16-byte reads at a 16-byte lane stride are free
+  // of bank conflicts; 4-byte reads at that stride are not).
+  u32x4 ra[4], rb[2];
+  // Stage ks = 4 n + k (k = ks % 4, a constant: the stage loop is unrolled by
+  // four) from ring slot k.
+  auto compute = [&](int ks, int k) {
+    const uint8_t* as = a_st[k];
+    const uint8_t* bs = b_st[k];
     // scale bytes of K blocks 4 ks + fh (sub-step 0: byte 0 after the shift)
     // and 4 ks + 2 + fh (sub-step 1: byte 2, picked with op_sel); blocks past
     // K (whose codes load as zero) get the neutral byte 127; only the last
     // stage can be a tail stage, and only when K / 32 is not a multiple of 4
-    const int grp = (ks >> 2) & 1, wsel = 4 * (ks & 3);
+    const int grp = (ks >> 2) & 1;
     const bool tail = 4 * ks + 4 > kblocks;  // uniform
     auto fix = [&](unsigned w, bool last_row, unsigned patch) {
       if (tail && last_row) w = patch;
@@ -213,12 +220,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     // Every LDS read of the stage is issued before the first MFMA, each into
     // registers of its own, so the reads overlap one another and the MFMAs
     // wait only for the operands they take.
-    unsigned wa[4], wb[2];
     u32x4 va[2][4], vb[2][2];
+    if (k == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) wa[i] = *reinterpret_cast<const unsigned*>(&as_st[grp][16 * (128 * wm + 32 * i + fr) + wsel]);
+      for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const u32x4*>(&as_st[grp][16 * (128 * wm + 32 * i + fr)]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) wb[j] = *reinterpret_cast<const unsigned*>(&bs_st[grp][16 * (64 * wn + 32 * j + fr) + wsel]);
+      for (int j = 0; j < 2; ++j) rb[j] = *reinterpret_cast<const u32x4*>(&bs_st[grp][16 * (64 * wn + 32 * j + fr)]);
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int c = 2 * s + fh;
@@ -236,9 +244,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     __builtin_amdgcn_sched_barrier(0);
     int sa[4], sb[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sa[i] = fix(wa[i], m0 + 128 * wm + 32 * i + fr == g.M - 1, pa);
+    for (int i = 0; i < 4; ++i) sa[i] = fix(ra[i][k], m0 + 128 * wm + 32 * i + fr == g.M - 1, pa);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) sb[j] = fix(wb[j], n0 + 64 * wn + 32 * j + fr == g.N - 1, pb);
+    for (int j = 0; j < 2; ++j) sb[j] = fix(rb[j][k], n0 + 64 * wn + 32 * j + fr == g.N - 1, pb);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -259,19 +267,26 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   // operations, may stay outstanding), barrier, load stage ks + 3 into the
   // slot stage ks - 1 used (every wave is past it), multiply stage ks.
   // Stages past the end load nothing but zeros.
-  issue(0, 0);
-  issue(1, 1);
-  issue(2, 2);
-  for (int ks = 0; ks < nsteps; ++ks) {
-    // loads issued after stage ks's: stages ks + 1 and ks + 2 (8 code loads),
-    // plus one scale load for each of them that opens a stage group
-    if (((ks + 1) & 3) == 0 || ((ks + 2) & 3) == 0)  // uniform
-      __builtin_amdgcn_s_waitcnt((9 & 15) | ((9 >> 4) << 14) | 0x70 | 0xF00);  // vmcnt(9)
-    else
-      __builtin_amdgcn_s_waitcnt((8 & 15) | ((8 >> 4) << 14) | 0x70 | 0xF00);  // vmcnt(8)
-    lds_barrier();
-    issue(ks + 3, (ks + 3) & 3);
-    compute(ks, ks & 3);
+  issue(0, 0, true);
+  issue(1, 1, false);
+  issue(2, 2, false);
+  for (int ks0 = 0; ks0 < nsteps; ks0 += 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int ks = ks0 + k;
+      if (ks < nsteps) {  // uniform
+        // loads issued after stage ks's: stages ks + 1 and ks + 2 (8 code
+        // loads), plus the scale load of stage ks + 1 or ks + 2 when one of
+        // them opens a stage group (k = 3, 2)
+        if (k >= 2)
+          __builtin_amdgcn_s_waitcnt((9 & 15) | ((9 >> 4) << 14) | 0x70 | 0xF00);  // vmcnt(9)
+        else
+          __builtin_amdgcn_s_waitcnt((8 & 15) | ((8 >> 4) << 14) | 0x70 | 0xF00);  // vmcnt(8)
+        lds_barrier();
+        issue(ks + 3, (k + 3) & 3, k == 1);
+        compute(ks, k);
+      }
+    }
   }
   // no load into LDS may still be in flight when the workgroup ends
   __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);
