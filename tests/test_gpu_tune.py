@@ -52,3 +52,30 @@ def test_tune_records_and_reproduces(T, d):
     assert kq.kq_auto_variant(T, d, True, False) == kq.KQ_MFMA_OTF
     kq.kq_tune_reset()
     assert kq.kq_auto_variant(T, d, True, True) == kq.KQ_MFMA_OTF
+
+
+@pytest.mark.parametrize("T,d", [(4096, 2240), (8192, 1152), (300, 3072)])
+def test_tuned_grid_split_leaves_results_unchanged(T, d):
+    """kq_tune also picks the size of the MFMA kernel's second grid part; the
+    outputs after tuning are bit-identical to the untuned ones (the split only
+    decides which workgroup computes a tile)."""
+    kq.kq_tune_reset()
+    X = synth.random_matrix(T, d, seed=3 * T + d, n_outliers=d // 50, mult=80.0)
+    P = synth.random_params(d // 32, seed=d + 7)
+    Xd, Pd = dev(X), dev(P)
+    Kbf = torch.empty((d // 32, 3, 32, 32), dtype=torch.int16, device="cuda:0")
+    kq.kq_build_blocks(Pd, d // 32, None, Kbf, 3)
+    ref = {}
+    for v in (kq.KQ_MFMA_OTF, kq.KQ_MFMA_DENSE):
+        c, s = kq.alloc_outputs(Xd)
+        kq.kq_quantize_ex(Xd, Pd if v == kq.KQ_MFMA_OTF else None, 15, Kbf if v == kq.KQ_MFMA_DENSE else None, v, c, s)
+        ref[v] = (c, s)
+    codes, scales = kq.alloc_outputs(Xd)
+    v = kq.kq_tune(Xd, Pd, Kbf, codes, scales, reps=3)
+    c2, s2 = kq.alloc_outputs(Xd)
+    kq.kq_quantize_ex(Xd, Pd, 15, Kbf, kq.KQ_AUTO, c2, s2)
+    torch.cuda.synchronize()
+    if v in ref:
+        assert torch.equal(codes, ref[v][0]) and torch.equal(scales, ref[v][1])
+        assert torch.equal(c2, ref[v][0]) and torch.equal(s2, ref[v][1])
+    kq.kq_tune_reset()

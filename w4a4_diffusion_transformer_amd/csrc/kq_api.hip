@@ -2,6 +2,7 @@
 // The declarations and the contract are in include/kq.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdlib>
 #include <cmath>
@@ -66,11 +67,18 @@ const Overrides& overrides() {
   return o;
 }
 
+// Size of the MFMA kernel's second grid part: percent of the tiles and
+// tiles per workgroup, -1 for the built-in rule.
+struct Split {
+  int tail_pct = -1, n2 = -1;
+};
+
 // Choices recorded by kq_tune, keyed by shape and the inputs supplied.
 struct Tuned {
   int64_t tokens, d;
   bool has_params, has_split;
   int variant;
+  Split split;
 };
 
 std::mutex& tuned_mutex() {
@@ -83,21 +91,23 @@ std::vector<Tuned>& tuned_table() {
   return table;
 }
 
-int tuned_lookup(int64_t tokens, int64_t d, bool has_params, bool has_split) {
+// The recorded choice for this key, or variant KQ_AUTO when there is none.
+Tuned tuned_lookup(int64_t tokens, int64_t d, bool has_params, bool has_split) {
   std::lock_guard<std::mutex> lock(tuned_mutex());
   for (const Tuned& t : tuned_table())
-    if (t.tokens == tokens && t.d == d && t.has_params == has_params && t.has_split == has_split) return t.variant;
-  return KQ_AUTO;
+    if (t.tokens == tokens && t.d == d && t.has_params == has_params && t.has_split == has_split) return t;
+  return Tuned{tokens, d, has_params, has_split, KQ_AUTO, Split{}};
 }
 
-void tuned_store(int64_t tokens, int64_t d, bool has_params, bool has_split, int variant) {
+void tuned_store(int64_t tokens, int64_t d, bool has_params, bool has_split, int variant, Split split) {
   std::lock_guard<std::mutex> lock(tuned_mutex());
   for (Tuned& t : tuned_table())
     if (t.tokens == tokens && t.d == d && t.has_params == has_params && t.has_split == has_split) {
       t.variant = variant;
+      t.split = split;
       return;
     }
-  tuned_table().push_back(Tuned{tokens, d, has_params, has_split, variant});
+  tuned_table().push_back(Tuned{tokens, d, has_params, has_split, variant, split});
 }
 
 // KQ_AUTO: a KQ_VARIANT override when its inputs are present; else the
@@ -108,7 +118,7 @@ void tuned_store(int64_t tokens, int64_t d, bool has_params, bool has_split, int
 int auto_variant(int64_t tokens, int64_t d, bool has_params, bool has_split) {
   const int o = overrides().variant;
   if (o > 0 && (o == KQ_MFMA_DENSE ? has_split : has_params)) return o;
-  const int t = tuned_lookup(tokens, d, has_params, has_split);
+  const int t = tuned_lookup(tokens, d, has_params, has_split).variant;
   if (t != KQ_AUTO) return t;
   if (has_params) return KQ_MFMA_OTF;
   if (has_split) return KQ_MFMA_DENSE;
@@ -132,9 +142,12 @@ struct Mod {
   int64_t tps;
 };
 
+// split: the MFMA kernel's grid split; nullptr takes the one kq_tune recorded
+// for this shape and variant (plain quantize calls only), else the rule.
 kq_status run(int front, const uint16_t* X, int64_t tokens, int64_t d, const float* P, int64_t pstride,
               const uint16_t* Kbf, int variant, const float* m, float* Y, uint8_t* codes, uint8_t* scales,
-              hipStream_t stream, const Mod* mod = nullptr, int hblock = 32, bool check_only = false) {
+              hipStream_t stream, const Mod* mod = nullptr, int hblock = 32, bool check_only = false,
+              const Split* split = nullptr) {
   kq_status st = check_shape(tokens, d);
   if (st != KQ_OK) return st;
   if (front < kq::FRONT_KRON || front > kq::FRONT_HADAMARD) return KQ_ERR_VARIANT;
@@ -199,6 +212,15 @@ kq_status run(int front, const uint16_t* X, int64_t tokens, int64_t d, const flo
       a.mshift = mod->mshift;
       a.tps = (int)(mod->tps < tokens ? mod->tps : tokens);
     }
+    Split sp;
+    if (split) {
+      sp = *split;
+    } else if (!mod && !Y && pstride == 15) {
+      const Tuned t = tuned_lookup(tokens, d, P != nullptr, Kbf != nullptr);
+      if (t.variant == variant) sp = t.split;
+    }
+    a.req_tail_pct = sp.tail_pct;
+    a.req_n2 = sp.n2;
     return from_hip(
         kq::launch_mfma(variant == KQ_MFMA_OTF ? KSRC_PARAMS : KSRC_SPLIT, Y != nullptr, mod != nullptr, a, stream));
   }
@@ -431,15 +453,25 @@ kq_status kq_tune(const uint16_t* X, int64_t tokens, int64_t d, const float* K_p
     if (chosen) *chosen = (kq_variant)auto_variant(tokens, d, K_params != nullptr, K_bf16 != nullptr);
     return KQ_OK;
   }
-  int cands[3];
+  // Candidates: each variant the inputs allow; the MFMA variants also with
+  // several sizes of the grid's second part (the built-in rule first).
+  static const Split kSplits[] = {{-1, -1}, {6, 1}, {12, 2}, {12, 3}, {18, 2}, {18, 4}, {25, 4}};
+  constexpr int kNS = (int)(sizeof(kSplits) / sizeof(kSplits[0]));
+  struct Cand {
+    int variant;
+    Split split;
+  };
+  Cand cands[2 * kNS + 1];
   int nc = 0;
-  if (K_params) cands[nc++] = KQ_MFMA_OTF;
-  if (K_bf16) cands[nc++] = KQ_MFMA_DENSE;
-  if (K_params) cands[nc++] = KQ_BUTTERFLY;
+  if (K_params)
+    for (const Split& sp : kSplits) cands[nc++] = Cand{KQ_MFMA_OTF, sp};
+  if (K_bf16)
+    for (const Split& sp : kSplits) cands[nc++] = Cand{KQ_MFMA_DENSE, sp};
+  if (K_params) cands[nc++] = Cand{KQ_BUTTERFLY, Split{}};
   // argument checks of every candidate before any HIP call
   for (int i = 0; i < nc; ++i) {
-    st = run(kq::FRONT_KRON, X, tokens, d, K_params, 15, K_bf16, cands[i], nullptr, nullptr, out_codes, out_scales,
-             stream, nullptr, 32, true);
+    st = run(kq::FRONT_KRON, X, tokens, d, K_params, 15, K_bf16, cands[i].variant, nullptr, nullptr, out_codes,
+             out_scales, stream, nullptr, 32, true, &cands[i].split);
     if (st != KQ_OK) return st;
   }
   hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -448,38 +480,49 @@ kq_status kq_tune(const uint16_t* X, int64_t tokens, int64_t d, const float* K_p
     (void)hipEventDestroy(e0);
     return KQ_ERR_HIP;
   }
-  int best = cands[0];
-  float best_ms = 0.0f;
+  // Three rounds over all candidates (interleaved, so that a clock change
+  // during the tuning does not favour one of them); each candidate is
+  // scored by its median round.
+  constexpr int kRounds = 3;
+  float ms[kRounds][2 * kNS + 1] = {};
   st = KQ_OK;
-  for (int i = 0; i < nc && st == KQ_OK; ++i) {
-    auto once = [&]() {
-      return run(kq::FRONT_KRON, X, tokens, d, K_params, 15, K_bf16, cands[i], nullptr, nullptr, out_codes, out_scales,
-                 stream);
-    };
-    for (int w = 0; w < 3 && st == KQ_OK; ++w) st = once();  // warm-up
-    if (st != KQ_OK) break;
-    if (hipEventRecord(e0, stream) != hipSuccess) { st = KQ_ERR_HIP; break; }
-    for (int r = 0; r < reps && st == KQ_OK; ++r) st = once();
-    if (st != KQ_OK) break;
-    float ms = 0.0f;
-    if (hipEventRecord(e1, stream) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
-        hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
-      st = KQ_ERR_HIP;
-      break;
-    }
-    if (i == 0 || ms < best_ms) {
-      best = cands[i];
-      best_ms = ms;
+  for (int r = 0; r < kRounds && st == KQ_OK; ++r) {
+    for (int i = 0; i < nc && st == KQ_OK; ++i) {
+      auto once = [&]() {
+        return run(kq::FRONT_KRON, X, tokens, d, K_params, 15, K_bf16, cands[i].variant, nullptr, nullptr, out_codes,
+                   out_scales, stream, nullptr, 32, false, &cands[i].split);
+      };
+      for (int w = 0; w < 3 && st == KQ_OK; ++w) st = once();  // warm-up
+      if (st != KQ_OK) break;
+      if (hipEventRecord(e0, stream) != hipSuccess) { st = KQ_ERR_HIP; break; }
+      for (int k = 0; k < reps && st == KQ_OK; ++k) st = once();
+      if (st != KQ_OK) break;
+      if (hipEventRecord(e1, stream) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+          hipEventElapsedTime(&ms[r][i], e0, e1) != hipSuccess) {
+        st = KQ_ERR_HIP;
+        break;
+      }
     }
   }
   (void)hipEventDestroy(e0);
   (void)hipEventDestroy(e1);
   if (st != KQ_OK) return st;
-  tuned_store(tokens, d, K_params != nullptr, K_bf16 != nullptr, best);
-  if (chosen) *chosen = (kq_variant)best;
+  int best = 0;
+  float best_ms = 0.0f;
+  for (int i = 0; i < nc; ++i) {
+    float v[kRounds];
+    for (int r = 0; r < kRounds; ++r) v[r] = ms[r][i];
+    std::sort(v, v + kRounds);
+    if (i == 0 || v[kRounds / 2] < best_ms) {
+      best = i;
+      best_ms = v[kRounds / 2];
+    }
+  }
+  tuned_store(tokens, d, K_params != nullptr, K_bf16 != nullptr, cands[best].variant, cands[best].split);
+  if (chosen) *chosen = (kq_variant)cands[best].variant;
   // leave the chosen variant's result in the outputs
-  return run(kq::FRONT_KRON, X, tokens, d, K_params, 15, K_bf16, best, nullptr, nullptr, out_codes, out_scales,
-             stream);
+  return run(kq::FRONT_KRON, X, tokens, d, K_params, 15, K_bf16, cands[best].variant, nullptr, nullptr, out_codes,
+             out_scales, stream, nullptr, 32, false, &cands[best].split);
 }
 
 void kq_tune_reset(void) {

@@ -34,6 +34,10 @@ struct MfmaArgs {
   int tps;
   int ngroups, nchunks;
   int w1, r1, n2;  // second part of the grid: see above
+  // requested size of the second part of the grid (percent of the tiles,
+  // tiles per workgroup); -1: the built-in rule.  The results do not depend
+  // on it, only the time.
+  int req_tail_pct = -1, req_n2 = -1;
 };
 
 // Row-segment decomposition of the vector-ALU kernels: a workgroup of four
