@@ -199,17 +199,19 @@ kq_status kq_build_blocks16(const float* K_params16, int64_t nb16, float* K_f32,
 /*
  * Per-shape tuning of KQ_AUTO (opt-in).  Times every variant the supplied
  * inputs allow (KQ_MFMA_OTF and KQ_BUTTERFLY need K_params with stride 15,
- * KQ_MFMA_DENSE needs K_bf16), the MFMA variants each with seven sizes of
- * the second part of their grid (the share of row tiles left to workgroups
- * that start as others finish, and the tiles each of those takes; outputs do
- * not depend on it), on the caller's buffers: three interleaved rounds of
+ * KQ_MFMA_DENSE needs K_bf16), the MFMA variants each with fourteen grid
+ * shapes (seven sizes of the second part of the grid, the share of row tiles
+ * left to workgroups that start as others finish and the tiles each of those
+ * takes, times a first part sized for the resident workgroups per CU or for
+ * one; outputs do not depend on the grid shape), on the caller's buffers:
+ * three interleaved rounds of
  * 3 warm-up launches and `reps` timed launches per candidate
  * (1 <= reps <= 1000, else KQ_ERR_SHAPE), timed with events on `stream`,
  * each candidate scored by its median round.  The fastest is recorded for
  * (tokens, d, which inputs are supplied), process-wide: later KQ_AUTO calls
  * with that key use its variant (kq_auto_variant reports it; a KQ_VARIANT
  * environment override still wins), and later kq_quantize / kq_quantize_ex
- * calls with that key, stride 15 and that variant use its grid split.  On return out_codes / out_scales hold the chosen variant's result
+ * calls with that key, stride 15 and that variant use its grid shape.  On return out_codes / out_scales hold the chosen variant's result
  * and *chosen (if not NULL) the variant.  This is the one entry point that
  * blocks: it synchronizes on its timing event.  Neither input -> KQ_ERR_VARIANT;
  * other errors as kq_quantize_ex; a failed launch or event -> KQ_ERR_HIP.

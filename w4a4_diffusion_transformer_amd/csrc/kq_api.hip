@@ -67,10 +67,11 @@ const Overrides& overrides() {
   return o;
 }
 
-// Size of the MFMA kernel's second grid part: percent of the tiles and
-// tiles per workgroup, -1 for the built-in rule.
+// Grid shape of the MFMA kernel: size of its second part (percent of the
+// tiles, tiles per workgroup) and the workgroups per CU its first part is
+// sized for; -1 for the built-in rule.
 struct Split {
-  int tail_pct = -1, n2 = -1;
+  int tail_pct = -1, n2 = -1, wg_per_cu = -1;
 };
 
 // Choices recorded by kq_tune, keyed by shape and the inputs supplied.
@@ -221,6 +222,7 @@ kq_status run(int front, const uint16_t* X, int64_t tokens, int64_t d, const flo
     }
     a.req_tail_pct = sp.tail_pct;
     a.req_n2 = sp.n2;
+    a.req_wg_per_cu = sp.wg_per_cu;
     return from_hip(
         kq::launch_mfma(variant == KQ_MFMA_OTF ? KSRC_PARAMS : KSRC_SPLIT, Y != nullptr, mod != nullptr, a, stream));
   }
@@ -297,8 +299,10 @@ int resident_per_cu(const void* fn, int block_threads) {
   return cap > 0 && cap < value ? cap : value;
 }
 
-int chunks_one_round(const void* fn, int block_threads, int ngroups, int ntiles) {
-  const int64_t slots = (int64_t)cu_count() * resident_per_cu(fn, block_threads);
+int chunks_one_round(const void* fn, int block_threads, int ngroups, int ntiles, int wg_per_cu_cap) {
+  int per_cu = resident_per_cu(fn, block_threads);
+  if (wg_per_cu_cap > 0 && wg_per_cu_cap < per_cu) per_cu = wg_per_cu_cap;
+  const int64_t slots = (int64_t)cu_count() * per_cu;
   int64_t ch = slots / ngroups;
   if (ch > ntiles) ch = ntiles;
   if (ch < 1) ch = 1;
@@ -454,8 +458,11 @@ kq_status kq_tune(const uint16_t* X, int64_t tokens, int64_t d, const float* K_p
     return KQ_OK;
   }
   // Candidates: each variant the inputs allow; the MFMA variants also with
-  // several sizes of the grid's second part (the built-in rule first).
-  static const Split kSplits[] = {{-1, -1}, {6, 1}, {12, 2}, {12, 3}, {18, 2}, {18, 4}, {25, 4}};
+  // several sizes of the grid's second part, each with the first part sized
+  // for the resident workgroups per CU or for one (the built-in rule first).
+  static const Split kSplits[] = {{-1, -1, -1}, {6, 1, -1}, {12, 2, -1}, {12, 3, -1}, {18, 2, -1}, {18, 4, -1},
+                                  {25, 4, -1},  {-1, -1, 1}, {6, 1, 1},   {12, 2, 1},  {12, 3, 1},  {18, 2, 1},
+                                  {18, 4, 1},   {25, 4, 1}};
   constexpr int kNS = (int)(sizeof(kSplits) / sizeof(kSplits[0]));
   struct Cand {
     int variant;

@@ -34,10 +34,10 @@ struct MfmaArgs {
   int tps;
   int ngroups, nchunks;
   int w1, r1, n2;  // second part of the grid: see above
-  // requested size of the second part of the grid (percent of the tiles,
-  // tiles per workgroup); -1: the built-in rule.  The results do not depend
-  // on it, only the time.
-  int req_tail_pct = -1, req_n2 = -1;
+  // requested grid shape: size of the second part (percent of the tiles,
+  // tiles per workgroup) and workgroups per CU the first part is sized for;
+  // -1: the built-in rule.  The results do not depend on it, only the time.
+  int req_tail_pct = -1, req_n2 = -1, req_wg_per_cu = -1;
 };
 
 // Row-segment decomposition of the vector-ALU kernels: a workgroup of four
@@ -68,7 +68,7 @@ int cu_count();
 int resident_per_cu(const void* fn, int block_threads);
 // Row chunks so that ngroups x nchunks workgroups fill the machine exactly
 // once (no second, partial round), with at least one row tile per chunk.
-int chunks_one_round(const void* fn, int block_threads, int ngroups, int ntiles);
+int chunks_one_round(const void* fn, int block_threads, int ngroups, int ntiles, int wg_per_cu_cap = 0);
 
 hipError_t launch_mfma(int ksrc, bool store_y, bool mod, const MfmaArgs& args, hipStream_t stream);
 hipError_t launch_quad(int front, bool store_y, const QuadArgs& args, hipStream_t stream);

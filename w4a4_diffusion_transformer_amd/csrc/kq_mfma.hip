@@ -427,7 +427,7 @@ hipError_t launch_mfma(int ksrc, bool store_y, bool mod, const MfmaArgs& args, h
   MfmaArgs a = args;
   const int nt = (a.T + kRows - 1) / kRows;
   a.ngroups = (a.nb + kCB - 1) / kCB;
-  a.nchunks = chunks_one_round(fn, kThreads, a.ngroups, nt);
+  a.nchunks = chunks_one_round(fn, kThreads, a.ngroups, nt, a.req_wg_per_cu);
   // Second part of the grid (tiles from r1 on, n2 per workgroup), sized by
   // the tiles a first-part workgroup would otherwise take (measured on
   // MI355X: finish times of equal first-part workgroups spread by up to a
