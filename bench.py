@@ -214,7 +214,10 @@ def gemm_table(kq, torch, np, dev):
     """The W4A4 consumer GEMM (kq_gemm_mx, MXFP4 x MXFP4 -> bf16) at DiT linear-layer shapes:
     FLUX.1-schnell MLP fc1 / fc2 and attention qkv at 4608 tokens, PixArt-Sigma MLP fc1 at 2 x 4096
     tokens.  Operands are random codes with scales in [2^-9, 2^6]; the time does not depend on values.
-    TFLOP/s counts 2 M N K; the roofline peak is MI355X's dense FP4 figure, 10.1 PFLOP/s."""
+    TFLOP/s counts 2 M N K; the roofline peak is MI355X's dense FP4 figure, 10.1 PFLOP/s.
+    Beside it, the ROCm library's MXFP4 GEMM on the same operands (hipBLASLt through
+    torch._scaled_mm, E8M0 block scales, bf16 out), timed the same way, when this torch build
+    offers it; the bf16 outputs of the two are compared too (largest difference in bf16 steps)."""
     out = {}
     L = kq.lib()
     stream = torch.cuda.current_stream().cuda_stream
@@ -245,8 +248,69 @@ def gemm_table(kq, torch, np, dev):
         tf = 2.0 * M * N * K / sec / 1e12
         out[name] = {"M": M, "N": N, "K": K, "us": round(sec * 1e6, 1), "TFLOPs": round(tf, 1),
                      "frac_fp4_peak": round(tf / 10100.0, 4)}
+        out[name]["hipblaslt_mxfp4"] = library_mxfp4(torch, a, asc, b, bsc, y, M, N, K, sec)
         print(f"# gemm {name}: {out[name]}", file=sys.stderr, flush=True)
     return out
+
+
+def library_mxfp4(torch, a, asc, b, bsc, y, M, N, K, kq_sec):
+    """hipBLASLt's MXFP4 GEMM (torch._scaled_mm) on the same operands; None if unavailable."""
+    f4, e8 = getattr(torch, "float4_e2m1fn_x2", None), getattr(torch, "float8_e8m0fnu", None)
+    if f4 is None or e8 is None:
+        return None
+
+    def call():
+        return torch._scaled_mm(a.view(f4), b.view(f4).t(), scale_a=asc.view(e8), scale_b=bsc.view(e8),
+                                out_dtype=torch.bfloat16)
+
+    try:
+        yl = None
+        for _ in range(2):  # the first call can fail while the library's kernel generator initialises
+            try:
+                yl = call()
+                torch.cuda.synchronize()
+                break
+            except RuntimeError:
+                yl = None
+        if yl is None:
+            return None
+        # bf16 steps between the two outputs (order-preserving integer map of the bf16 bit patterns)
+        def key(t):
+            i = t.view(torch.int16).to(torch.int32)
+            return torch.where(i < 0, -32768 - i, i)
+        steps = int((key(yl) - key(y)).abs().max().item())
+        # one timed call first: where the library takes far longer than this kernel (it took
+        # seconds per call at K = 1152 on MI355X), that single call is the figure reported
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        torch.cuda.synchronize()
+        one = e0.elapsed_time(e1) * 1e-3
+        if one > 20 * kq_sec:
+            return {"us": round(one * 1e6, 1), "TFLOPs": round(2.0 * M * N * K / one / 1e12, 1),
+                    "kq_time_over_library_time": round(kq_sec / one, 4), "max_bf16_steps_apart": steps,
+                    "reps": 1}
+        t_warm = time.perf_counter() + 0.1
+        while time.perf_counter() < t_warm:
+            call()
+            torch.cuda.synchronize()
+        reps = 20
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) * 1e-3 / reps
+        return {"us": round(sec * 1e6, 1), "TFLOPs": round(2.0 * M * N * K / sec / 1e12, 1),
+                "kq_time_over_library_time": round(kq_sec / sec, 3), "max_bf16_steps_apart": steps,
+                "reps": reps}
+    except RuntimeError as e:
+        print(f"# hipBLASLt MXFP4 unavailable: {str(e)[:120]}", file=sys.stderr, flush=True)
+        return None
 
 
 def parse():
