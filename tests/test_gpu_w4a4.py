@@ -154,6 +154,24 @@ def test_gemm_full_size_sampled_rows():
     assert np.all(err <= 1e-5 * bound + 1e-30), float((err / bound).max())
 
 
+def test_gemm_whole_and_half_tiles():
+    """4352 x 4096 output: 272 tiles of 256 x 256 on 256 compute units, so the
+    first 256 run whole and the 16 of the last, partial round (the band of
+    rows 4096 .. 4351) run as two 128-row halves each; rows of both kinds
+    checked against the oracle, every column."""
+    M, N, K = 4352, 4096, 256
+    ac, as_ = random_mx(M, K, seed=81)
+    bc, bs = random_mx(N, K, seed=82)
+    y, yb = run_gemm(ac, as_, bc, bs)
+    rng = np.random.default_rng(83)
+    rows = np.concatenate([rng.choice(4096, size=48, replace=False), np.arange(4096, M, 5), [M - 1]])
+    ref = oracle.gemm_mx(ac[rows], as_[rows], bc, bs)
+    bound = gemm_bound(ac[rows], as_[rows], bc, bs)
+    err = np.abs(host(y)[rows].astype(np.float64) - ref)
+    assert np.all(err <= 1e-5 * bound + 1e-30), float((err / np.maximum(bound, 1e-300)).max())
+    np.testing.assert_array_equal(host(yb.view(torch.int16)), host(y.to(torch.bfloat16).view(torch.int16)))
+
+
 def test_gemm_errors():
     ac, as_ = random_mx(8, 64, seed=1)
     with pytest.raises(ValueError):

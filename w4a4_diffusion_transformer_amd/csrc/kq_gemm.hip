@@ -15,16 +15,18 @@
 // exact; sums are fp32.
 //
 // Workgroup: 8 waves (2 along M x 4 along N), a 256 x 256 tile of Y, each
-// wave 128 x 64 (4 x 2 MFMA tiles of 32 x 32).  K advances 128 per stage.
+// wave 128 x 64 (4 x 2 MFMA tiles of 32 x 32), or, for the tiles of a
+// partial last round of the GPU, a 128 x 256 half tile (waves of 64 x 64).
+// K advances 128 per stage.
 // The A and B stage tiles (256 rows x 64 B each) go from global memory
 // straight into LDS (buffer loads with the LDS bit), in a ring of four
 // stages: three are in flight while one is multiplied.  Scale bytes go the
 // same way, 16 K blocks (four stages) of a row per 16-byte load, into a ring
 // of two such groups.  Rows of a staged tile are 64 B; the 16-byte chunk c
 // of row r sits at position c ^ ((r / 4) % 4), so that the 16 rows one
-// fragment read touches at a fixed chunk fall on distinct banks.  Rows past M or N and K blocks past K
-// load as zero codes (buffer range / out-of-range offsets), which add
-// nothing.
+// fragment read touches at a fixed chunk fall on distinct banks.  Rows past
+// M or N and K blocks past K load as zero codes (buffer range /
+// out-of-range offsets), which add nothing.
 #include "kq_device.hpp"
 #include "kq_internal.h"
 
@@ -91,68 +93,62 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(1024))) uint8_t a_st[kStages][kTileB];
-  __shared__ __attribute__((aligned(1024))) uint8_t b_st[kStages][kTileB];
-  __shared__ __attribute__((aligned(256))) uint8_t as_st[2][kScB];  // by parity of the stage group
-  __shared__ __attribute__((aligned(256))) uint8_t bs_st[2][kScB];
-
+// One output tile of 64 MI rows x 256 columns at (m0, n0): MI = 4 is the
+// whole 256 x 256 tile, MI = 2 half of one (see launch_gemm).  Each wave
+// computes 32 MI rows x 64 columns (MI x 2 MFMA tiles of 32 x 32).
+template <int MI>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, int m0, int n0, uint8_t (&a_st)[kStages][kTileB],
+                                          uint8_t (&b_st)[kStages][kTileB], uint8_t (&as_st)[2][kScB],
+                                          uint8_t (&bs_st)[2][kScB]) {
+  constexpr int BM = 64 * MI;   // rows of the tile
+  constexpr int NA = MI / 2;    // 16-row groups of A each wave stages per stage
+  constexpr int kOps = NA + 2;  // code loads per wave and stage
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wv >> 2, wn = wv & 3;
-  // Tile of this workgroup: the tiles are numbered in groups of kGroupM M
-  // tiles, column by column; XCD x (workgroups are dealt to the eight XCDs
-  // in turn) takes the x-th eighth of that order, so the workgroups running
-  // at once on one XCD share A rows and B rows in its L2.
-  int tm, tn;
-  {
-    const int gm = (g.M + kBM - 1) / kBM, gn = (g.N + kBN - 1) / kBN;
-    const int t = xcd_remap((int)blockIdx.x, gm * gn);
-    const int per_group = kGroupM * gn;
-    const int grp = t / per_group, first = grp * kGroupM;
-    const int rows = min(kGroupM, gm - first);
-    const int w = t - grp * per_group;
-    tm = first + w % rows;
-    tn = w / rows;
-  }
-  const int m0 = tm * kBM, n0 = tn * kBN;
   const int K = g.K, kbytes = K >> 1, kblocks = K >> 5;
   const int nsteps = (K + 127) >> 7;
-  const int mrows = min(kBM, g.M - m0), nrows = min(kBN, g.N - n0);
+  const int mrows = min(BM, g.M - m0), nrows = min(kBN, g.N - n0);
 
-  // Code loads of one stage: this wave moves the 16-row groups 2 wv and
-  // 2 wv + 1 of A and of B (lane l -> row l / 4 of the group, LDS position
-  // l % 4, holding chunk (l % 4) ^ ((l / 16) % 4)).  Scale loads, once per
-  // group of 4 stages: wave w < 4 moves the 16 scale bytes (K blocks of the
-  // 4 stages) of A rows 64 w .. 64 w + 63, wave w >= 4 those of B rows
-  // 64 (w - 4) ..; one 16-byte load per lane and row (byte offsets need no
-  // alignment for these loads: checked on MI355X).  The code descriptors
-  // cover only the rows a load may touch; the scale descriptors run to the
-  // end of the scale tensor, since a row's last 16-byte piece reaches into
-  // the next row.  A dword that crosses the end of a range reads as zero
-  // (range checks are per dword: checked on MI355X), so when K / 32 is not a
-  // multiple of 4 the final (K / 32) % 4 scale bytes of the last row of A
-  // and of B are read here with ordinary loads and patched in at the last
-  // stage.
-  u32x4 da[2], db[2], dsc;
+  // Code loads of one stage: this wave moves the NA 16-row groups NA wv ..
+  // of A and the groups 2 wv, 2 wv + 1 of B (lane l -> row l / 4 of the
+  // group, LDS position l % 4, holding chunk (l % 4) ^ ((l / 16) % 4)).
+  // Scale loads, once per group of 4 stages: wave w < 4 moves the 16 scale
+  // bytes (K blocks of the 4 stages) of A rows 64 w .. 64 w + 63 (none past
+  // the tile: a zero range), wave w >= 4 those of B rows 64 (w - 4) ..; one
+  // 16-byte load per lane and row (byte offsets need no alignment for these
+  // loads: checked on MI355X).  The code descriptors cover only the rows a
+  // load may touch; the scale descriptors run to the end of the scale
+  // tensor, since a row's last 16-byte piece reaches into the next row.  A
+  // dword that crosses the end of a range reads as zero (range checks are
+  // per dword: checked on MI355X), so when K / 32 is not a multiple of 4 the
+  // final (K / 32) % 4 scale bytes of the last row of A and of B are read
+  // here with ordinary loads and patched in at the last stage.
+  u32x4 da[NA], db[2], dsc;
   const int cchunk = (lane & 3) ^ ((lane >> 4) & 3);
+#pragma unroll
+  for (int k = 0; k < NA; ++k) {
+    const int G = NA * wv + k;
+    const int ra = min(16, max(0, mrows - 16 * G));
+    da[k] = desc_uniform(g.a_codes + (int64_t)(m0 + 16 * G) * kbytes, (int64_t)ra * kbytes);
+  }
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int G = 2 * wv + k;
-    const int ra = min(16, max(0, mrows - 16 * G)), rb = min(16, max(0, nrows - 16 * G));
-    da[k] = desc_uniform(g.a_codes + (int64_t)(m0 + 16 * G) * kbytes, (int64_t)ra * kbytes);
+    const int rb = min(16, max(0, nrows - 16 * G));
     db[k] = desc_uniform(g.b_codes + (int64_t)(n0 + 16 * G) * kbytes, (int64_t)rb * kbytes);
   }
   {
     const bool sa_side = wv < 4;  // wave-uniform
     const int r0 = 64 * (wv & 3);
-    const int rs = max(0, (sa_side ? g.M - m0 : g.N - n0) - r0);  // rows to the end of the tensor
-    dsc = sa_side ? desc_uniform(g.a_scales + (int64_t)(m0 + r0) * kblocks, (int64_t)rs * kblocks)
+    const int rs = sa_side ? (r0 < BM ? max(0, g.M - m0 - r0) : 0)  // rows to the end of the tensor
+                           : max(0, g.N - n0 - r0);
+    dsc = sa_side ? desc_uniform(g.a_scales + (int64_t)(m0 + min(r0, BM)) * kblocks, (int64_t)rs * kblocks)
                   : desc_uniform(g.b_scales + (int64_t)(n0 + r0) * kblocks, (int64_t)rs * kblocks);
   }
   const int kfull = kblocks & ~3, kr = kblocks & 3;
   unsigned pa = 0, pb = 0;  // final partial scale dwords of rows M - 1 and N - 1
-  if (kr != 0 && m0 + kBM >= g.M) {
+  if (kr != 0 && m0 + BM >= g.M) {
     const uint8_t* p = g.a_scales + (int64_t)(g.M - 1) * kblocks + kfull;
     for (int j = 0; j < kr; ++j) pa |= (unsigned)p[j] << (8 * j);
   }
@@ -163,17 +159,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   const uint32_t crow_off = (uint32_t)((lane >> 2) * kbytes);
   const uint32_t srow_off = (uint32_t)(lane * kblocks);
 
-  // Vector memory operations this wave issues for stage ks: 4 code loads,
+  // Vector memory operations this wave issues for stage ks: kOps code loads,
   // plus the scale load of the stage group when ks opens one.
   auto issue = [&](int ks, int slot, bool opens_group) {
     const bool cin = ks * 128 + 32 * cchunk < K;
     const uint32_t co = cin ? crow_off + (uint32_t)(64 * ks + 16 * cchunk) : kOut;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int G = 2 * wv + k;
-      dma_b128(da[k], co, lds_addr(&a_st[slot][1024 * G]));
-      dma_b128(db[k], co, lds_addr(&b_st[slot][1024 * G]));
-    }
+    for (int k = 0; k < NA; ++k) dma_b128(da[k], co, lds_addr(&a_st[slot][1024 * (NA * wv + k)]));
+#pragma unroll
+    for (int k = 0; k < 2; ++k) dma_b128(db[k], co, lds_addr(&b_st[slot][1024 * (2 * wv + k)]));
     if (opens_group) {  // ks % 4 == 0
       const int p = ks >> 2;
       const uint32_t so = 16 * p < kblocks ? srow_off + (uint32_t)(16 * p) : kOut;
@@ -182,9 +176,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     }
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[MI][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -193,10 +187,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   // Fragment rows of this lane and its K half within a 64-K sub-step.
   const int fr = lane & 31, fh = lane >> 5;
   // Scale rows of the current stage group (16 bytes: 4 per stage) of this
-  // lane's A rows 128 wm + 32 i + fr and B rows 64 wn + 32 j + fr, read once
-  // per group as whole rows (16-byte reads at a 16-byte lane stride are free
-  // of bank conflicts; 4-byte reads at that stride are not).
-  u32x4 ra[4], rb[2];
+  // lane's A rows 32 MI wm + 32 i + fr and B rows 64 wn + 32 j + fr, read
+  // once per group as whole rows (16-byte reads at a 16-byte lane stride are
+  // free of bank conflicts; 4-byte reads at that stride are not).
+  u32x4 ra[MI], rb[2];
   // Stage ks = 4 n + k (k = ks % 4, a constant: the stage loop is unrolled by
   // four) from ring slot k.
   auto compute = [&](int ks, int k) {
@@ -220,10 +214,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     // Every LDS read of the stage is issued before the first MFMA, each into
     // registers of its own, so the reads overlap one another and the MFMAs
     // wait only for the operands they take.
-    u32x4 va[2][4], vb[2][2];
+    u32x4 va[2][MI], vb[2][2];
     if (k == 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ra[i] = *reinterpret_cast<const u32x4*>(&as_st[grp][16 * (128 * wm + 32 * i + fr)]);
+      for (int i = 0; i < MI; ++i)
+        ra[i] = *reinterpret_cast<const u32x4*>(&as_st[grp][16 * (32 * MI * wm + 32 * i + fr)]);
 #pragma unroll
       for (int j = 0; j < 2; ++j) rb[j] = *reinterpret_cast<const u32x4*>(&bs_st[grp][16 * (64 * wn + 32 * j + fr)]);
     }
@@ -231,8 +226,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
     for (int s = 0; s < 2; ++s) {
       const int c = 2 * s + fh;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int R = 128 * wm + 32 * i + fr;
+      for (int i = 0; i < MI; ++i) {
+        const int R = 32 * MI * wm + 32 * i + fr;
         va[s][i] = *reinterpret_cast<const u32x4*>(&as[64 * R + 16 * (c ^ ((R >> 2) & 3))]);
       }
 #pragma unroll
@@ -242,15 +237,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    int sa[4], sb[2];
+    int sa[MI], sb[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sa[i] = fix(ra[i][k], m0 + 128 * wm + 32 * i + fr == g.M - 1, pa);
+    for (int i = 0; i < MI; ++i) sa[i] = fix(ra[i][k], m0 + 32 * MI * wm + 32 * i + fr == g.M - 1, pa);
 #pragma unroll
     for (int j = 0; j < 2; ++j) sb[j] = fix(rb[j][k], n0 + 64 * wn + 32 * j + fr == g.N - 1, pb);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           if (s == 0)
@@ -263,25 +258,27 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   };
 
   // Stages 0 .. 2 in flight; per stage ks: wait until this wave's loads of
-  // stage ks have landed (the loads of stages ks + 1 and ks + 2, 16
-  // operations, may stay outstanding), barrier, load stage ks + 3 into the
-  // slot stage ks - 1 used (every wave is past it), multiply stage ks.
-  // Stages past the end load nothing but zeros.
+  // stage ks have landed (the loads of stages ks + 1 and ks + 2 may stay
+  // outstanding), barrier, load stage ks + 3 into the slot stage ks - 1 used
+  // (every wave is past it), multiply stage ks.  Stages past the end load
+  // nothing but zeros.
   issue(0, 0, true);
   issue(1, 1, false);
   issue(2, 2, false);
+  // loads issued after stage ks's: those of stages ks + 1 and ks + 2 (2 kOps
+  // code loads), plus the scale load of stage ks + 1 or ks + 2 when one of
+  // them opens a stage group (k = 3, 2)
+  constexpr int w01 = 2 * kOps, w23 = 2 * kOps + 1;
+  static_assert(w23 < 16, "vmcnt field");
   for (int ks0 = 0; ks0 < nsteps; ks0 += 4) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int ks = ks0 + k;
       if (ks < nsteps) {  // uniform
-        // loads issued after stage ks's: stages ks + 1 and ks + 2 (8 code
-        // loads), plus the scale load of stage ks + 1 or ks + 2 when one of
-        // them opens a stage group (k = 3, 2)
         if (k >= 2)
-          __builtin_amdgcn_s_waitcnt((9 & 15) | ((9 >> 4) << 14) | 0x70 | 0xF00);  // vmcnt(9)
+          __builtin_amdgcn_s_waitcnt(w23 | 0x70 | 0xF00);
         else
-          __builtin_amdgcn_s_waitcnt((8 & 15) | ((8 >> 4) << 14) | 0x70 | 0xF00);  // vmcnt(8)
+          __builtin_amdgcn_s_waitcnt(w01 | 0x70 | 0xF00);
         lds_barrier();
         issue(ks + 3, (k + 3) & 3, k == 1);
         compute(ks, k);
@@ -291,12 +288,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   // no load into LDS may still be in flight when the workgroup ends
   __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);
 
-  // Y rows m0 + 128 wm + 32 i + 8 (r / 4) + 4 fh + r % 4, columns n0 + 64 wn + 32 j + fr; one
+  // Y rows m0 + 32 MI wm + 32 i + 8 (r / 4) + 4 fh + r % 4, columns n0 + 64 wn + 32 j + fr; one
   // descriptor per 32-row band (ranges stay far below 2^31 bytes for any N).
   const int64_t N = g.N;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int band = 128 * wm + 32 * i;
+  for (int i = 0; i < MI; ++i) {
+    const int band = 32 * MI * wm + 32 * i;
     const int brows = min(32, max(0, mrows - band));
     const int64_t base = (int64_t)(m0 + band) * N;
     if (g.y_f32) {
@@ -329,11 +326,57 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
   }
 }
 
+// Tiles of Y (256 x 256) are numbered in groups of kGroupM M tiles, column
+// by column.  Workgroups below full_tiles each compute one whole tile; the
+// tiles from full_tiles on (the last, partial round of the GPU) are each
+// computed as two 128-row halves by two workgroups, so that round takes
+// about half as long.  Each kind is spread over the eight XCDs (workgroups
+// are dealt to them in turn) so that XCD x takes the x-th eighth of its
+// range of the order, and the workgroups running at once on one XCD share A
+// rows and B rows in its L2.
+__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs g) {
+  __shared__ __attribute__((aligned(1024))) uint8_t a_st[kStages][kTileB];
+  __shared__ __attribute__((aligned(1024))) uint8_t b_st[kStages][kTileB];
+  __shared__ __attribute__((aligned(256))) uint8_t as_st[2][kScB];  // by parity of the stage group
+  __shared__ __attribute__((aligned(256))) uint8_t bs_st[2][kScB];
+
+  const int gm = (g.M + kBM - 1) / kBM, gn = (g.N + kBN - 1) / kBN;
+  const int b = (int)blockIdx.x;
+  const bool whole = b < g.full_tiles;  // workgroup-uniform
+  int t, half = 0;
+  if (whole) {
+    t = xcd_remap(b, g.full_tiles);
+  } else {
+    // full_tiles is a multiple of 8, so block b - full_tiles sits on XCD (b - full_tiles) % 8
+    const int u = xcd_remap(b - g.full_tiles, 2 * (gm * gn - g.full_tiles));
+    t = g.full_tiles + (u >> 1);
+    half = u & 1;
+  }
+  const int per_group = kGroupM * gn;
+  const int grp = t / per_group, first = grp * kGroupM;
+  const int rows = min(kGroupM, gm - first);
+  const int w = t - grp * per_group;
+  const int tm = first + w % rows, tn = w / rows;
+  if (whole)
+    gemm_tile<4>(g, tm * kBM, tn * kBN, a_st, b_st, as_st, bs_st);
+  else
+    gemm_tile<2>(g, tm * kBM + 128 * half, tn * kBN, a_st, b_st, as_st, bs_st);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream) {
   GemmArgs g = args;
-  const dim3 grid((unsigned)(((g.N + kBN - 1) / kBN) * ((g.M + kBM - 1) / kBM)));
+  // Wave quantisation: with `slots` workgroups resident at once, the tiles
+  // past the last whole multiple of `slots` run as a partial last round.
+  // When that round fills at most half the slots, its tiles are computed as
+  // two halves each (twice the workgroups, each half the work).
+  const int64_t tiles = (int64_t)((g.N + kBN - 1) / kBN) * ((g.M + kBM - 1) / kBM);
+  const int64_t slots = (int64_t)cu_count() * resident_per_cu((const void*)&gemm_kernel, kThreads);
+  const int64_t rem = tiles % slots;
+  const bool split = rem > 0 && 2 * rem <= slots && (tiles - rem) % 8 == 0;
+  g.full_tiles = (int)(split ? tiles - rem : tiles);
+  const dim3 grid((unsigned)(split ? tiles + rem : tiles));
   void* kargs[] = {&g};
   return hipLaunchKernel((const void*)&gemm_kernel, grid, dim3(kThreads), kargs, 0, stream);
 }

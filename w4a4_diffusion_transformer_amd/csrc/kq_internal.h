@@ -82,6 +82,7 @@ struct GemmArgs {
   int M, N, K;
   float* y_f32;
   uint16_t* y_bf16;
+  int full_tiles;  // set by launch_gemm: tiles computed whole; the rest in two halves
 };
 
 hipError_t launch_gemm(const GemmArgs& args, hipStream_t stream);
