@@ -59,7 +59,10 @@ def shape_table(kq, torch, np, synth, dev):
     and outputs) exceeds 512 MB, twice the Infinity Cache, and calls cycle
     through the copies back to back on one stream."""
     out = {}
-    for spec in [s_ for c in (1, 2, 3) for s_ in synth.CONFIGS[c]]:
+    # plus the shard one GPU of an 8-way tensor-parallel FLUX.1-schnell MLP fc2 input would hold
+    # (X2's 12288 channels split in eight 32-aligned slices: 4608 x 1536), same distribution as X2
+    shard = synth.MatrixSpec("flux_x2_tp8_shard", 4608, 1536, 3, 3, synth.BASE_NORMAL, 0.005, 100.0, 1.0)
+    for spec in [s_ for c in (1, 2, 3) for s_ in synth.CONFIGS[c]] + [shard]:
         X = synth.matrix(spec)
         P = synth.params(spec)
         m = synth.smooth_mult(X)

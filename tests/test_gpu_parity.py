@@ -365,7 +365,9 @@ def test_error_codes_on_device_buffers():
 # ---------------------------------------------------------------- full-size workloads
 
 
-FULL = [s for c in (1, 2, 3, 4) for s in synth.CONFIGS[c]]
+# plus one GPU's shard of an 8-way tensor-parallel FLUX X2 (4608 x 1536, X2's distribution)
+FULL = [s for c in (1, 2, 3, 4) for s in synth.CONFIGS[c]] + [
+    synth.MatrixSpec("flux_x2_tp8_shard", 4608, 1536, 3, 3, synth.BASE_NORMAL, 0.005, 100.0, 1.0)]
 
 
 @pytest.mark.parametrize("spec", FULL, ids=lambda s: s.name)
