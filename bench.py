@@ -100,7 +100,7 @@ def shape_table(kq, torch, np, synth, dev):
         if not spec.shared_k:
             # kq_tune's pick for this shape (K_params and the dense split both supplied; kq_tune takes
             # per-block parameters only), then timed through KQ_AUTO
-            tuned = kq.kq_tune(Xs[0], Pd, Kbf, *outs[0], reps=10)
+            tuned = kq.kq_tune(Xs[0], Pd, Kbf, *outs[0], reps=30)
             row["tuned_variant"] = kq.variant_name(tuned)
             calls["kroquant_tuned"] = (L.kq_quantize_ex,
                                        lambda i: (xs[i], T, d, pp, 15, kp, kq.KQ_AUTO, *os_[i], stream))
