@@ -220,7 +220,8 @@ def gemm_table(kq, torch, np, dev):
     TFLOP/s counts 2 M N K; the roofline peak is MI355X's dense FP4 figure, 10.1 PFLOP/s.
     Beside it, the ROCm library's MXFP4 GEMM on the same operands (hipBLASLt through
     torch._scaled_mm, E8M0 block scales, bf16 out), timed the same way, when this torch build
-    offers it; the bf16 outputs of the two are compared too (largest difference in bf16 steps)."""
+    offers it; the bf16 outputs of the two are compared too (largest difference in bf16 steps).
+    And the bf16 GEMM of the same shape, the layer W4A4 replaces."""
     out = {}
     L = kq.lib()
     stream = torch.cuda.current_stream().cuda_stream
@@ -252,8 +253,32 @@ def gemm_table(kq, torch, np, dev):
         out[name] = {"M": M, "N": N, "K": K, "us": round(sec * 1e6, 1), "TFLOPs": round(tf, 1),
                      "frac_fp4_peak": round(tf / 10100.0, 4)}
         out[name]["hipblaslt_mxfp4"] = library_mxfp4(torch, a, asc, b, bsc, y, M, N, K, sec)
+        out[name]["bf16_matmul"] = bf16_matmul(torch, dev, M, N, K, sec)
         print(f"# gemm {name}: {out[name]}", file=sys.stderr, flush=True)
     return out
+
+
+def bf16_matmul(torch, dev, M, N, K, kq_sec):
+    """The same layer in bf16 (what W4A4 replaces): torch.matmul of X [M][K] and the weight stored
+    transposed and contiguous [K][N] (hipBLASLt), timed like the GEMM above."""
+    x = torch.randn((M, K), dtype=torch.bfloat16, device=dev)
+    wt = torch.randn((K, N), dtype=torch.bfloat16, device=dev).contiguous()
+    yb = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    t_warm = time.perf_counter() + 0.1
+    while time.perf_counter() < t_warm:
+        torch.matmul(x, wt, out=yb)
+        torch.cuda.synchronize()
+    reps = 20
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(x, wt, out=yb)
+    e1.record()
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) * 1e-3 / reps
+    return {"us": round(sec * 1e6, 1), "TFLOPs": round(2.0 * M * N * K / sec / 1e12, 1),
+            "kq_time_over_bf16_time": round(kq_sec / sec, 3)}
 
 
 def library_mxfp4(torch, a, asc, b, bsc, y, M, N, K, kq_sec):
