@@ -142,19 +142,22 @@ __device__ __forceinline__ void setup_a(bf16x8 A[2][3], const Params15& pv, cons
 // scale by the row statistics, times (1 + scale[c]), plus shift[c]; then
 // rounded to bf16 (nearest even).  The transform then sees exactly the bf16
 // activation an unfused LayerNorm + modulation kernel would have written.
-__device__ __forceinline__ bf16x8 modulate8(bf16x8 x, float mean, float rstd, bool norm, const float opa[8],
-                                            bool has_scale, const float sh[8], bool has_shift) {
+// A step whose input is absent gets an identity operand instead of a branch
+// (mean +0, rstd 1, scale factor 1, shift -0: x - 0, x * 1 and x + (-0) are
+// x exactly, signed zeros included), so the four operations run
+// unconditionally (as selects, the skipped steps had cost three more
+// instructions per value).
+__device__ __forceinline__ bf16x8 modulate8(bf16x8 x, float mean, float rstd, const float opa[8],
+                                            const float sh[8]) {
 #pragma clang fp contract(off)
   bf16x8 out;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     float v = (float)x[i];
-    if (norm) {
-      v = v - mean;
-      v = v * rstd;
-    }
-    if (has_scale) v = v * opa[i];
-    if (has_shift) v = v + sh[i];
+    v = v - mean;
+    v = v * rstd;
+    v = v * opa[i];
+    v = v + sh[i];
     out[i] = (__bf16)v;
   }
   return out;
@@ -305,11 +308,25 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(MfmaArgs a) {
       const int smp = crow / a.tps;
       if (smp != cur_s) {  // wave-uniform; a few times per workgroup at most
         cur_s = smp;
+        // four 16-byte loads under one wait: the wait also drains the X
+        // tiles in flight (the load counter retires in order), so it must
+        // come once per sample change, not once per value
         const int64_t off = (int64_t)smp * a.d + 32 * j + 8 * q;
+        f32x4 m0 = {0.f, 0.f, 0.f, 0.f}, m1 = m0, h0 = {-0.f, -0.f, -0.f, -0.f}, h1 = h0;
+        if (a.mscale) {  // uniform
+          m0 = *reinterpret_cast<const f32x4*>(a.mscale + off);
+          m1 = *reinterpret_cast<const f32x4*>(a.mscale + off + 4);
+        }
+        if (a.mshift) {  // uniform
+          h0 = *reinterpret_cast<const f32x4*>(a.mshift + off);
+          h1 = *reinterpret_cast<const f32x4*>(a.mshift + off + 4);
+        }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          opa[i] = a.mscale ? 1.0f + a.mscale[off + i] : 1.0f;
-          sh[i] = a.mshift ? a.mshift[off + i] : 0.0f;
+        for (int i = 0; i < 4; ++i) {
+          opa[i] = 1.0f + m0[i];
+          opa[4 + i] = 1.0f + m1[i];
+          sh[i] = h0[i];
+          sh[4 + i] = h1[i];
         }
       }
     }
@@ -320,8 +337,9 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(MfmaArgs a) {
       const int tr = 16 * rt + tl;
       bf16x8 xb = *reinterpret_cast<const bf16x8*>(&lds_in[buf][tr * kInStride + 64 * jl + 16 * q]);
       if constexpr (MOD) {
-        xb = modulate8(xb, __uint_as_float(cst[rt][0]), __uint_as_float(cst[rt][1]), a.stats != nullptr, opa,
-                       a.mscale != nullptr, sh, a.mshift != nullptr);
+        const bool norm = a.stats != nullptr;  // uniform
+        xb = modulate8(xb, norm ? __uint_as_float(cst[rt][0]) : 0.0f, norm ? __uint_as_float(cst[rt][1]) : 1.0f,
+                       opa, sh);
         // the exact path reads the block back from this tile
         *reinterpret_cast<bf16x8*>(&lds_in[buf][tr * kInStride + 64 * jl + 16 * q]) = xb;
       }
