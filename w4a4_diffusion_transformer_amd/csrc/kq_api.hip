@@ -460,8 +460,8 @@ kq_status kq_tune(const uint16_t* X, int64_t tokens, int64_t d, const float* K_p
   // Candidates: each variant the inputs allow; the MFMA variants also with
   // several sizes of the grid's second part, each with the first part sized
   // for the resident workgroups per CU or for one (the built-in rule first).
-  static const Split kSplits[] = {{-1, -1, -1}, {6, 1, -1}, {12, 2, -1}, {12, 3, -1}, {18, 2, -1}, {18, 4, -1},
-                                  {25, 4, -1},  {-1, -1, 1}, {6, 1, 1},   {12, 2, 1},  {12, 3, 1},  {18, 2, 1},
+  static const Split kSplits[] = {{-1, -1, -1}, {9, 1, -1}, {12, 2, -1}, {12, 3, -1}, {18, 2, -1}, {18, 4, -1},
+                                  {25, 4, -1},  {-1, -1, 1}, {9, 1, 1},   {12, 2, 1},  {12, 3, 1},  {18, 2, 1},
                                   {18, 4, 1},   {25, 4, 1}};
   constexpr int kNS = (int)(sizeof(kSplits) / sizeof(kSplits[0]));
   struct Cand {

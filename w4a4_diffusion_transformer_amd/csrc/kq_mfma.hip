@@ -459,9 +459,11 @@ hipError_t launch_mfma(int ksrc, bool store_y, bool mod, const MfmaArgs& args, h
   // fifth of the kernel, with the slow ones tied to address ranges).
   const int per = (nt + a.nchunks - 1) / a.nchunks;
   // (at 24 or more tiles per workgroup, 12% in runs of 3 measured 0.9-1.5% faster on the stress
-  // matrix than 18% in runs of 6, in two sweeps with non-overlapping ranges)
+  // matrix than 18% in runs of 6, in two sweeps with non-overlapping ranges; below 8, single
+  // tiles measured 6-8% faster than runs of 2 at PixArt X1 and SANA X1, two sweeps, equal at
+  // FLUX X1)
   const int tail_pct = a.req_tail_pct >= 0 ? std::min(a.req_tail_pct, 50) : (per >= 8 ? 12 : 6);
-  a.n2 = a.req_n2 > 0 ? std::min(a.req_n2, 64) : (per >= 24 ? 3 : (per >= 8 ? 4 : 2));
+  a.n2 = a.req_n2 > 0 ? std::min(a.req_n2, 64) : (per >= 24 ? 3 : (per >= 8 ? 4 : 1));
   const int n1 = std::max(1, (int)((int64_t)nt * (100 - tail_pct) / (100 * (int64_t)a.nchunks)));
   a.r1 = (int)std::min<int64_t>(nt, (int64_t)n1 * a.nchunks);
   a.w1 = a.ngroups * a.nchunks;
