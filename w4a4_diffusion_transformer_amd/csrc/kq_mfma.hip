@@ -467,7 +467,13 @@ hipError_t launch_mfma(int ksrc, bool store_y, bool mod, const MfmaArgs& args, h
   const int n1 = std::max(1, (int)((int64_t)nt * (100 - tail_pct) / (100 * (int64_t)a.nchunks)));
   a.r1 = (int)std::min<int64_t>(nt, (int64_t)n1 * a.nchunks);
   a.w1 = a.ngroups * a.nchunks;
-  const int64_t w2 = (int64_t)a.ngroups * ((nt - a.r1 + a.n2 - 1) / a.n2);
+  int64_t w2 = (int64_t)a.ngroups * ((nt - a.r1 + a.n2 - 1) / a.n2);
+  // a launch holds fewer than 2^32 work-items: longer runs where a requested
+  // split would exceed that (matrices of some 10^11 elements)
+  while ((a.w1 + w2) * kThreads >= (int64_t(1) << 32)) {
+    a.n2 *= 2;
+    w2 = (int64_t)a.ngroups * ((nt - a.r1 + a.n2 - 1) / a.n2);
+  }
   // Three tiles ahead when a first-part workgroup has at most four tiles
   // (measured on MI355X: 9% faster at FLUX X1, 16% at PixArt X1; 1-4% slower
   // with more tiles per workgroup).  Both forms fit two workgroups per CU.
