@@ -136,3 +136,36 @@ def test_row_stats_and_adaln_past_4gib(big):
         oracle.adaln_rows(Xrows[i:i + 1], ref_st[i:i + 1], sc[r // TPS:r // TPS + 1], sh[r // TPS:r // TPS + 1],
                           tokens_per_sample=1) for i, r in enumerate(ROWS)])
     check("adaln", oracle.KRON, Xmod, codes, scales, P=P)
+
+
+def test_gemm_past_4gib():
+    """Y [66000 x 32768]: the fp32 output passes byte 2^32 at row 32768, the
+    bf16 one at row 65536; the last tile row is partial (66000 = 257 x 256 + 208).
+    Random MXFP4 operands (K = 64), sampled rows, every column, against the
+    oracle: |Y - exact| <= 1e-5 sum|a b|, bf16 = nearest-even rounding of the fp32."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    M, N, K = 66000, 32768, 64
+    rng = np.random.default_rng(71)
+    ac = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    as_ = rng.integers(118, 136, size=(M, K // 32), dtype=np.uint8)
+    bc = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    bs = rng.integers(118, 136, size=(N, K // 32), dtype=np.uint8)
+    t = lambda a: torch.from_numpy(a).to("cuda:0")
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda:0")
+    yb = torch.empty((M, N), dtype=torch.bfloat16, device="cuda:0")
+    kq.kq_gemm_mx(t(ac), t(as_), t(bc), t(bs), y, yb)
+    torch.cuda.synchronize()
+    rows = sorted({0, 32767, 32768, 32769, 65535, 65536, 65537, 65791, 65792, 65999}
+                  | {int(r) for r in rng.choice(M, 12, replace=False)})
+    got = y[rows].cpu().numpy().astype(np.float64)
+    gotb = yb[rows].view(torch.int16).cpu().numpy()
+    del y, yb
+    torch.cuda.empty_cache()
+    ref = oracle.gemm_mx(ac[rows], as_[rows], bc, bs)
+    A = np.abs(oracle.dequant_rows(ac[rows], as_[rows]))
+    B = np.abs(oracle.dequant_rows(bc, bs))
+    bound = A @ B.T
+    err = np.abs(got - ref)
+    assert np.all(err <= 1e-5 * bound + 1e-30), float((err / np.maximum(bound, 1e-300)).max())
+    np.testing.assert_array_equal(gotb, torch.from_numpy(got.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy())
