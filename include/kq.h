@@ -148,6 +148,12 @@ kq_status kq_quantize_ex(const uint16_t* X, int64_t tokens, int64_t d, const flo
  * K_params and K_bf16 are supplied (nonzero = supplied): the same rule the
  * entry points apply.  Returns KQ_AUTO when no variant can serve the call
  * (neither input supplied).  Pure host logic, no HIP call.
+ *
+ * Two environment variables, read once at the first call, exist for
+ * measurement and change no result: KQ_VARIANT (mfma_dense, mfma_otf or
+ * butterfly) replaces KQ_AUTO's choice wherever the supplied inputs allow
+ * that variant, and KQ_WG_PER_CU (1 .. 64) caps the workgroups per compute
+ * unit that every grid of the library is sized for.  Other values are ignored.
  */
 kq_variant kq_auto_variant(int64_t tokens, int64_t d, int has_params, int has_split);
 
@@ -266,7 +272,9 @@ kq_status kq_row_stats(const uint16_t* X, int64_t tokens, int64_t d, float eps, 
  * per-channel scales and shifts; the form v (1 + scale) + shift is the DiT
  * one).  tokens_per_sample must be a multiple of 32 or at least tokens
  * (KQ_ERR_SHAPE otherwise).  Variants: KQ_AUTO, KQ_MFMA_OTF, KQ_MFMA_DENSE
- * with the same inputs as kq_quantize_ex; KQ_BUTTERFLY -> KQ_ERR_VARIANT.
+ * with the same inputs as kq_quantize_ex; KQ_BUTTERFLY -> KQ_ERR_VARIANT
+ * (KQ_AUTO never resolves to it here: where KQ_VARIANT or a kq_tune record
+ * names the butterfly, this entry point takes KQ_MFMA_OTF).
  * row_stats must be 8-byte aligned, mod_scale / mod_shift 4-byte aligned.
  */
 kq_status kq_quantize_adaln(const uint16_t* X, int64_t tokens, int64_t d, const float* row_stats,

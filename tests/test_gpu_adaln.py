@@ -184,3 +184,39 @@ def test_fused_error_codes():
     with pytest.raises(kq.KQError) as e:
         kq.kq_quantize_adaln(Xd, dev(st), dev(sc), dev(sh), 64, dev(P), codes, scales, 15, None, kq.KQ_BUTTERFLY)
     assert e.value.status == 4
+
+
+_CHILD = r"""
+import sys
+import numpy as np, torch
+sys.path.insert(0, sys.argv[1])
+import synth
+import w4a4_diffusion_transformer_amd as kq
+T, d = 96, 1152
+X = torch.from_numpy(synth.random_matrix(T, d, seed=3, n_outliers=12, mult=50.0, token_sigma=0.5).view(np.int16)).cuda()
+P = torch.from_numpy(synth.random_params(d // 32, seed=4)).cuda()
+sc, sh = (torch.from_numpy(a).cuda() for a in synth.adaln_vectors(1, d, seed=5))
+st = torch.empty((T, 2), dtype=torch.float32, device="cuda")
+kq.kq_row_stats(X, 1e-6, st)
+assert kq.kq_auto_variant(T, d, True, False) == kq.KQ_BUTTERFLY, "override not in effect"
+auto = kq.kq_quantize_adaln(X, st, sc, sh, T, P, *kq.alloc_outputs(X))
+otf = kq.kq_quantize_adaln(X, st, sc, sh, T, P, *kq.alloc_outputs(X), variant=kq.KQ_MFMA_OTF)
+plain = kq.kq_quantize_ex(X, P, 15, None, kq.KQ_AUTO, *kq.alloc_outputs(X))
+torch.cuda.synchronize()
+assert all(torch.equal(a, b) for a, b in zip(auto, otf)), "AUTO under the butterfly override differs from mfma_otf"
+assert not torch.equal(auto[0], plain[0]), "modulation not applied"
+print("ok")
+"""
+
+
+def test_auto_under_butterfly_override_keeps_the_producer_step():
+    """With KQ_VARIANT=butterfly (read once per process, hence a child
+    process), KQ_AUTO resolves to the butterfly for the plain quantizer, and the
+    fused AdaLN entry point, which has no butterfly form, takes mfma_otf: same
+    bytes as an explicit mfma_otf call, and not the unmodulated quantization."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, KQ_VARIANT="butterfly")
+    r = subprocess.run([sys.executable, "-c", _CHILD, root], env=env, capture_output=True, text=True, timeout=180)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout[-2000:] + r.stderr[-2000:]

@@ -166,7 +166,13 @@ kq_status run(int front, const uint16_t* X, int64_t tokens, int64_t d, const flo
   if (!X || !codes || !scales) return KQ_ERR_NULL;
   if (front == kq::FRONT_SMOOTH && !m) return KQ_ERR_NULL;
   if (front == kq::FRONT_KRON) {
-    if (variant == KQ_AUTO) variant = auto_variant(tokens, d, P != nullptr, Kbf != nullptr);
+    if (variant == KQ_AUTO) {
+      variant = auto_variant(tokens, d, P != nullptr, Kbf != nullptr);
+      // the producer step is fused into the MFMA kernels only: a butterfly
+      // choice (KQ_VARIANT, or a kq_tune record for this shape) yields to the
+      // K-from-scalars MFMA kernel, which takes the same inputs
+      if (mod && variant == KQ_BUTTERFLY) variant = KQ_MFMA_OTF;
+    }
     if (variant == KQ_MFMA_DENSE && !Kbf) return KQ_ERR_VARIANT;
     if (variant != KQ_MFMA_DENSE && !P) return KQ_ERR_VARIANT;
   }
