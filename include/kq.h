@@ -39,9 +39,9 @@
  *   ch_mult   fp32 [d] per-channel multipliers (SmoothQuant: 1/s_c).
  *   Y         fp32 [tokens][d], the values the quantizer rounded.
  *
- * Numerics.  The transform runs in fp32 (MFMA bf16 products of X with a
- * three-term bf16 split of K, or fp32 butterfly stages); the per-element
- * error against the exact sum is below 1e-5 of the block amax.  Whenever a
+ * Numerics.  The transform runs in fp32 (fp32 butterfly stages, or MFMA bf16
+ * products of X with a three-term bf16 split of K); the per-element error
+ * against the exact sum is below 1e-5 of the block amax.  Whenever a
  * block's amax lands within 2^-16 (relative) of a power of two, the columns
  * that decide the scale are recomputed exactly (fp64 sum of exact products,
  * the fp32 K), so the E8M0 scales equal those of an exact evaluation.  An
@@ -97,7 +97,8 @@ typedef enum {
   KQ_AUTO = 0,
   KQ_MFMA_DENSE = 1, /* MFMA bf16 contraction with prebuilt K_bf16 (three-term split) */
   KQ_MFMA_OTF = 2,   /* MFMA bf16 contraction, K rebuilt in-kernel from the 15 scalars */
-  KQ_BUTTERFLY = 3   /* five fp32 2x2 butterfly stages from the 15 scalars, no MFMA */
+  KQ_BUTTERFLY = 3   /* five fp32 butterfly stages (two shears each, then the product of the
+                        diagonals) from the 15 scalars, one block per lane, no MFMA */
 } kq_variant;
 
 /* Front-ends of kq_transform_f32. */
@@ -137,7 +138,8 @@ kq_status kq_quantize(const uint16_t* X, int64_t tokens, int64_t d, const float*
  * for every block).  K_bf16 (three-term split from kq_build_blocks, layout
  * above) is required by KQ_MFMA_DENSE and ignored by the other variants;
  * K_params is required by every variant except KQ_MFMA_DENSE.  KQ_AUTO uses
- * KQ_MFMA_DENSE when K_bf16 is given and K_params is NULL.
+ * KQ_BUTTERFLY when K_params is given and KQ_MFMA_DENSE when only K_bf16 is
+ * (unless kq_tune recorded another choice for the shape).
  */
 kq_status kq_quantize_ex(const uint16_t* X, int64_t tokens, int64_t d, const float* K_params,
                          int64_t params_block_stride, const uint16_t* K_bf16, kq_variant variant,
@@ -146,8 +148,10 @@ kq_status kq_quantize_ex(const uint16_t* X, int64_t tokens, int64_t d, const flo
 /*
  * The variant KQ_AUTO resolves to for a call with this shape, given whether
  * K_params and K_bf16 are supplied (nonzero = supplied): the same rule the
- * entry points apply.  Returns KQ_AUTO when no variant can serve the call
- * (neither input supplied).  Pure host logic, no HIP call.
+ * entry points apply (a KQ_VARIANT override, else a kq_tune record, else
+ * KQ_BUTTERFLY with K_params, KQ_MFMA_DENSE with K_bf16 alone).  Returns
+ * KQ_AUTO when no variant can serve the call (neither input supplied).  Pure
+ * host logic, no HIP call.
  *
  * Two environment variables, read once at the first call, exist for
  * measurement and change no result: KQ_VARIANT (mfma_dense, mfma_otf or
@@ -203,24 +207,29 @@ kq_status kq_build_blocks16(const float* K_params16, int64_t nb16, float* K_f32,
                             hipStream_t stream);
 
 /*
- * Per-shape tuning of KQ_AUTO (opt-in).  Times every variant the supplied
- * inputs allow (KQ_MFMA_OTF and KQ_BUTTERFLY need K_params with stride 15,
- * KQ_MFMA_DENSE needs K_bf16), the MFMA variants each with fourteen grid
- * shapes (seven sizes of the second part of the grid, the share of row tiles
- * left to workgroups that start as others finish and the tiles each of those
- * takes, times a first part sized for the resident workgroups per CU or for
- * one; outputs do not depend on the grid shape), on the caller's buffers:
- * three interleaved rounds of
- * 3 warm-up launches and `reps` timed launches per candidate
- * (1 <= reps <= 1000, else KQ_ERR_SHAPE), timed with events on `stream`,
- * each candidate scored by its median round.  The fastest is recorded for
- * (tokens, d, which inputs are supplied), process-wide: later KQ_AUTO calls
- * with that key use its variant (kq_auto_variant reports it; a KQ_VARIANT
- * environment override still wins), and later kq_quantize / kq_quantize_ex
- * calls with that key, stride 15 and that variant use its grid shape.  On return out_codes / out_scales hold the chosen variant's result
+ * Per-shape tuning of KQ_AUTO (opt-in).  Times the variant the built-in rule
+ * picks and every variant the supplied inputs allow (KQ_MFMA_OTF and
+ * KQ_BUTTERFLY need K_params with stride 15, KQ_MFMA_DENSE needs K_bf16), the
+ * MFMA variants each with fourteen grid shapes (seven sizes of the second
+ * part of the grid, the share of row tiles left to workgroups that start as
+ * others finish and the tiles each of those takes, times a first part sized
+ * for the resident workgroups per CU or for one; outputs do not depend on the
+ * grid shape), on the caller's buffers: three interleaved rounds of 3 warm-up
+ * launches and `reps` timed launches per candidate (1 <= reps <= 1000, else
+ * KQ_ERR_SHAPE), timed with events on `stream`, each candidate scored by its
+ * median round.  The fastest candidate is recorded if it is at least 3%
+ * faster than the built-in rule's, else the rule's choice is (the timing
+ * reuses one set of buffers, which can stay in the last-level cache; the
+ * margin keeps a pick that only wins warm from replacing the rule).  The
+ * record is keyed by (tokens, d, which inputs are supplied), process-wide:
+ * later KQ_AUTO calls with that key use its variant (kq_auto_variant reports
+ * it; a KQ_VARIANT environment override still wins), and later kq_quantize /
+ * kq_quantize_ex calls with that key, stride 15 and that variant use its grid
+ * shape.  On return out_codes / out_scales hold the recorded variant's result
  * and *chosen (if not NULL) the variant.  This is the one entry point that
- * blocks: it synchronizes on its timing event.  Neither input -> KQ_ERR_VARIANT;
- * other errors as kq_quantize_ex; a failed launch or event -> KQ_ERR_HIP.
+ * blocks: it synchronizes on its timing event.  Neither input ->
+ * KQ_ERR_VARIANT; other errors as kq_quantize_ex; a failed launch or event ->
+ * KQ_ERR_HIP.
  */
 kq_status kq_tune(const uint16_t* X, int64_t tokens, int64_t d, const float* K_params, const uint16_t* K_bf16,
                   uint8_t* out_codes, uint8_t* out_scales, int reps, kq_variant* chosen, hipStream_t stream);

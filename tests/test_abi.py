@@ -205,5 +205,5 @@ def test_tune_argument_checks(lib):
     assert t(A + 2, 4, 64, B, None, C, D, 5, ctypes.byref(chosen), None) == KQ_ERR_ALIGN
     assert t(A, 4, 64, B, None, A + 16, D, 5, ctypes.byref(chosen), None) == KQ_ERR_ALIAS
     assert t(A, 0, 64, B, None, C, D, 5, ctypes.byref(chosen), None) == KQ_OK
-    assert chosen.value == 2  # no tuning recorded: the default rule (mfma_otf)
+    assert chosen.value == 3  # no tuning recorded: the default rule (the butterfly kernel)
     lib.kq_tune_reset()

@@ -49,9 +49,9 @@ def test_tune_records_and_reproduces(T, d):
     assert torch.equal(codes, c2) and torch.equal(scales, s2)
     assert torch.equal(codes, c3) and torch.equal(scales, s3)
     # other keys keep the default rule
-    assert kq.kq_auto_variant(T, d, True, False) == kq.KQ_MFMA_OTF
+    assert kq.kq_auto_variant(T, d, True, False) == kq.KQ_BUTTERFLY
     kq.kq_tune_reset()
-    assert kq.kq_auto_variant(T, d, True, True) == kq.KQ_MFMA_OTF
+    assert kq.kq_auto_variant(T, d, True, True) == kq.KQ_BUTTERFLY
 
 
 @pytest.mark.parametrize("T,d", [(4096, 2240), (8192, 1152), (300, 3072)])

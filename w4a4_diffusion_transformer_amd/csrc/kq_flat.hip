@@ -1,0 +1,373 @@
+// Block-per-lane front-ends fused with the MXFP4 quantizer (gfx950).
+//
+// The activation X[T][d] is, in memory, a flat sequence of T * d/32 blocks
+// of 64 bytes (32 bf16 channels), and the codes and scales are flat
+// sequences of 16-byte and 1-byte block records in the same order.  A wave
+// takes a unit of 64 consecutive blocks (4 KB of X) at a time: four 1 KB
+// loads, each contiguous, land in a wave-private LDS region and are read
+// back so that lane i holds all 32 channels of block i of the unit.  The
+// whole transform, the block amax, the E8M0 byte and the E2M1 codes then
+// stay inside one lane, and the lane's 16 code bytes and its scale byte are
+// stored as one contiguous 1 KB + 64 B per wave.  No workgroup barrier: the
+// waves of a workgroup never share data.
+//
+// A wave visits units u0, u0 + P C, u0 + 2 P C, ... with P = nb / gcd(64, nb)
+// units spanning a whole number of rows, so lane i always holds the same
+// block column j = (64 u0 + i) mod nb and keeps that block's coefficients in
+// registers for all of its units.
+//
+// FRONT_KRON: y = x K(j), K = G1 (x) ... (x) G5 (KroQuant; Pith review,
+// "What carries the argument": the on-the-fly kernel that builds each block
+// from its 15 scalars).  Each factor
+//   G = [[1,0],[l,1]] [[a,b],[0,1/a]] = [[1,0],[l,1]] [[1,ab],[0,1]] diag(a,1/a)
+// splits into two shears and a diagonal.  By the mixed-product property
+// K = (L1 (x) ... (x) L5)(S1 (x) ... (x) S5)(D1 (x) ... (x) D5), and stages
+// acting on different channel bits commute, so for a row vector
+//   x K = [per factor k, on its bit p: x[c] += l x[c|p], then x[c|p] += ab x[c]
+//          for every c with bit p clear]  then  y[c] = x[c] * prod_k D_k[bit_k(c)],
+// five butterfly stages of one fused multiply-add per element, and one
+// multiply by the product of the five diagonals.  All in fp32; the error
+// against the exact sum stays well below 1e-5 of the block amax.
+// FRONT_PLAIN: y = x.  FRONT_SMOOTH: y = x * m[c].  FRONT_HADAMARD: the
+// 32-point Walsh-Hadamard butterflies, then / sqrt(32).
+#include "kq_device.hpp"
+#include "kq_internal.h"
+
+namespace kq {
+
+namespace {
+
+constexpr int kWaves = 4;             // waves per workgroup (independent)
+constexpr int kDepth = 2;             // units of loads in flight per wave
+constexpr int kUnitBlocks = 64;       // one block per lane
+constexpr int kUnitBytes = 64 * 64;   // bf16 bytes of a unit
+constexpr int kUnitCodes = 64 * 16;   // code bytes of a unit
+
+// Position (in 16-byte chunks) of quarter qq of block b of a unit in the
+// wave's LDS region.  The quarter index is XOR-swizzled with bits 2-3 of the
+// block so that the 1 KB writes (16 lanes: blocks 4k .. 4k+3, all quarters)
+// and the block reads (16 lanes: blocks 16k .. 16k+15, one quarter each)
+// both touch every 4-byte bank of a 256-byte line once.
+__device__ __forceinline__ int chunk_pos(int b, int qq) { return 4 * b + (qq ^ ((b >> 2) & 3)); }
+
+__device__ __forceinline__ float absmax32(const float y[32]) {
+  float m0 = fabsf(y[0]), m1 = fabsf(y[1]), m2 = fabsf(y[2]), m3 = fabsf(y[3]);
+#pragma unroll
+  for (int c = 4; c < 32; c += 8) {
+    m0 = fmaxf(m0, fmaxf(fabsf(y[c]), fabsf(y[c + 4])));
+    m1 = fmaxf(m1, fmaxf(fabsf(y[c + 1]), fabsf(y[c + 5])));
+    m2 = fmaxf(m2, fmaxf(fabsf(y[c + 2]), fabsf(y[c + 6])));
+    m3 = fmaxf(m3, fmaxf(fabsf(y[c + 3]), fabsf(y[c + 7])));
+  }
+  return fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+}
+
+// Maximum over the 32 lanes of each half of the wave (DPP within rows of
+// 16, then a swap between rows).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float max32(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror: lane i <-> 7 - i
+  v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror: lane i <-> 15 - i
+  const unsigned u = __float_as_uint(v);
+  const auto sw = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // rows 0 <-> 1, 2 <-> 3
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+// Exact quantization of block b of the staged unit, by the whole wave: a
+// block whose fp32 amax lies within 2^-16 of a power of two, where the
+// transform's rounding could decide the scale (rare).  Lane c (mod 32)
+// computes output channel c exactly, as the fp64 sum from +0 in input order
+// of the exact products x[r] K32[r][c] (KRON) or of (-1)^popcount(r & c) x[r]
+// then divided by sqrt(32) (HADAMARD), rounded once to fp32.  K32[r][c] is
+// the fp64 product, in factor order, of one entry per factor (G1 on bit 4),
+// rounded to fp32, with G = [[a, b], [l a, l b + 1/a]] in fp64: the block's
+// 15 scalars p15 and the five fp64 quotients 1/a come from LDS.  The block is
+// then quantized from these values: res receives its four code words and its
+// scale byte, ys (if not null) the 32 values.  Everything after the first
+// reads runs in registers, so that a wave meeting such a block is held up
+// only briefly.  Not inlined: the kernel's register allocation stays that of
+// its common path.
+template <int FRONT>
+__device__ __attribute__((noinline)) void exact_block(const uint8_t* stage, int b, const float* p15,
+                                                      const double* inv_a, int lane, unsigned* res, float* ys) {
+  const int c = lane & 31;
+  u32x4 w[4];
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq) w[qq] = *reinterpret_cast<const u32x4*>(stage + 16 * chunk_pos(b, qq));
+  auto x_of = [&](int r) {
+    const unsigned v = w[r >> 3][(r >> 1) & 3];
+    return (double)((r & 1) ? bf16_hi(v) : bf16_lo(v));
+  };
+  double s = 0.0;
+  if constexpr (FRONT == FRONT_KRON) {
+    double e0[5], e1[5];  // entries G_k[0][bit] and G_k[1][bit] of column c's bit of each factor
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      const double L = p15[3 * k], A = p15[3 * k + 1], B = p15[3 * k + 2];
+      const bool bit = (c >> (4 - k)) & 1;
+      e0[k] = bit ? B : A;
+      e1[k] = bit ? fma(L, B, inv_a[k]) : L * A;  // l b is exact in fp64: one rounding, as l b + 1/a
+    }
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      double p = ((r >> 4) & 1) ? e1[0] : e0[0];
+      p = p * (((r >> 3) & 1) ? e1[1] : e0[1]);
+      p = p * (((r >> 2) & 1) ? e1[2] : e0[2]);
+      p = p * (((r >> 1) & 1) ? e1[3] : e0[3]);
+      p = p * ((r & 1) ? e1[4] : e0[4]);
+      s = fma(x_of(r), (double)(float)p, s);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 32; ++r) s = s + ((__popc(r & c) & 1) ? -x_of(r) : x_of(r));
+  }
+  const float y = FRONT == FRONT_KRON ? (float)s : (float)(s / 5.6568542494923801952067548968387923142786875015078);
+  const unsigned byte = e8m0_byte(max32(fabsf(y)));
+  // channels 2q, 2q + 1 -> code byte q (even channel in the low nibble)
+  const float y1 = dpp_f<0xB1>(y);
+  const unsigned pair = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y, y1, __uint_as_float(byte << 23), 0) & 0xFFu;
+  if (lane < 32 && !(c & 1)) reinterpret_cast<uint8_t*>(res)[c >> 1] = (uint8_t)pair;
+  if (lane == 0) res[4] = byte;
+  if (ys && lane < 32) ys[c] = y;
+}
+
+template <int FRONT, bool STORE_Y>
+__global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
+  __shared__ __attribute__((aligned(256))) uint8_t lds_x[kWaves][kUnitBytes];
+  // exact path: each lane's 15 scalars and its five fp64 quotients 1/a
+  __shared__ float lds_p[FRONT == FRONT_KRON ? kWaves : 1][64][15];
+  __shared__ double lds_ia[FRONT == FRONT_KRON ? kWaves : 1][64][5];
+  constexpr bool kSum = FRONT == FRONT_KRON || FRONT == FRONT_HADAMARD;  // fronts with an exact path
+  __shared__ unsigned lds_res[kSum ? kWaves : 1][64][5];   // exact path: code words and byte per lane
+  __shared__ float lds_ys[kSum && STORE_Y ? kWaves : 1][32];  // exact path: the values (diagnostic Y)
+
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = __builtin_amdgcn_readfirstlane((int)blockIdx.x * kWaves + wv);
+  const int nph = a.phases;
+  if (gw >= nph * a.chunks) return;  // wave-uniform; nothing below synchronizes the workgroup
+  const int ph = gw % nph, chk = gw / nph;
+  const int64_t u0 = ph + (int64_t)nph * chk;         // first unit
+  const int64_t ustep = (int64_t)nph * a.chunks;      // units between this wave's units
+  const int n = u0 < a.units ? (int)((a.units - 1 - u0) / ustep) + 1 : 0;
+  if (n == 0) return;
+  const int j = (int)((64 * (int64_t)ph + lane) % a.nb);  // this lane's block column, for every unit
+  uint8_t* stage = lds_x[wv];
+
+  // ---- per-lane coefficients of block column j
+  float sl[5], ss[5], dg[32];  // KRON: shear l, shear a b (G1 .. G5), product of the diagonals
+  float mult[32];              // SMOOTH
+  if constexpr (FRONT == FRONT_KRON) {
+    const float* p = a.P + (int64_t)j * a.pstride;
+    float da[5], ia[5];
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      sl[k] = p[3 * k];
+      const float av = p[3 * k + 1], bv = p[3 * k + 2];
+      lds_p[wv][lane][3 * k] = sl[k];  // for the exact path
+      lds_p[wv][lane][3 * k + 1] = av;
+      lds_p[wv][lane][3 * k + 2] = bv;
+      lds_ia[wv][lane][k] = 1.0 / (double)av;
+      ss[k] = av * bv;
+      da[k] = av;
+      ia[k] = 1.0f / av;
+    }
+    // dg[c] = prod_k (bit (4 - k) of c ? 1/a_k : a_k), G1 first
+    float h2[4], h3[8], h4[16];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) h2[c] = ((c >> 1) ? ia[0] : da[0]) * ((c & 1) ? ia[1] : da[1]);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) h3[c] = h2[c >> 1] * ((c & 1) ? ia[2] : da[2]);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) h4[c] = h3[c >> 1] * ((c & 1) ? ia[3] : da[3]);
+#pragma unroll
+    for (int c = 0; c < 32; ++c) dg[c] = h4[c >> 1] * ((c & 1) ? ia[4] : da[4]);
+  }
+  if constexpr (FRONT == FRONT_SMOOTH) {
+    const f32x4* mp = reinterpret_cast<const f32x4*>(a.m + 32 * (int64_t)j);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const f32x4 v = mp[k];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mult[4 * k + i] = v[i];
+    }
+  }
+
+  // ---- wave-uniform cursors: the next unit to load, the unit being stored
+  const int64_t lstep = ustep * kUnitBytes;
+  const uint8_t* lx = reinterpret_cast<const uint8_t*>(a.X) + u0 * kUnitBytes;
+  int64_t lleft = a.xbytes - u0 * kUnitBytes;  // bytes from the load cursor to the end of X
+  auto clamp_bytes = [](int64_t left, int unit) { return left <= 0 ? 0 : (left >= unit ? unit : (int)left); };
+  u32x4 pre[kDepth][4];
+  auto load = [&](int slot) {
+    const auto rx = rsrc_uniform(lx, clamp_bytes(lleft, kUnitBytes));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      pre[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(1024 * i + 16 * lane), 0, kNT);
+    lx += lstep;
+    lleft -= lstep;
+  };
+  int64_t ub = u0 * kUnitBlocks;  // first block of the unit being computed
+  const int64_t bstep = ustep * kUnitBlocks;
+
+  auto compute = [&](int slot) {
+    // stage: 1 KB load i holds 16-byte chunk 64 i + lane = quarter (lane & 3) of block 16 i + lane / 4
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4*>(stage + 16 * chunk_pos(16 * i + (lane >> 2), lane & 3)) = pre[slot][i];
+    load(slot);  // the slot is free again: the loads of unit + kDepth go out now
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    u32x4 w[4];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) w[qq] = *reinterpret_cast<const u32x4*>(stage + 16 * chunk_pos(lane, qq));
+    float y[32];
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y[8 * qq + 2 * e] = bf16_lo(w[qq][e]);
+        y[8 * qq + 2 * e + 1] = bf16_hi(w[qq][e]);
+      }
+
+    if constexpr (FRONT == FRONT_KRON) {
+#pragma unroll
+      for (int k = 4; k >= 0; --k) {  // G5 (bit 0) first; the stages of different bits commute
+        const int bit = 1 << (4 - k);
+#pragma unroll
+        for (int c = 0; c < 32; ++c)
+          if (!(c & bit)) y[c] = fmaf(sl[k], y[c | bit], y[c]);
+#pragma unroll
+        for (int c = 0; c < 32; ++c)
+          if (!(c & bit)) y[c | bit] = fmaf(ss[k], y[c], y[c | bit]);
+      }
+#pragma unroll
+      for (int c = 0; c < 32; ++c) y[c] *= dg[c];
+    } else if constexpr (FRONT == FRONT_SMOOTH) {
+#pragma unroll
+      for (int c = 0; c < 32; ++c) y[c] *= mult[c];
+    } else if constexpr (FRONT == FRONT_HADAMARD) {
+#pragma unroll
+      for (int bit = 1; bit < 32; bit <<= 1)
+#pragma unroll
+        for (int c = 0; c < 32; ++c)
+          if (!(c & bit)) {
+            const float u = y[c], v = y[c | bit];
+            y[c] = u + v;
+            y[c | bit] = u - v;
+          }
+#pragma unroll
+      for (int c = 0; c < 32; ++c) y[c] *= 0.17677669529663688110021109052621225982120698f;  // 1/sqrt(32)
+    }
+
+    const float amax = absmax32(y);
+    unsigned byte = e8m0_byte(amax);
+    u32x4 cw;
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) cw[qq] = pack_fp4(&y[8 * qq], byte);
+    if constexpr (kSum) {
+      if (amax == 0.0f) cw = u32x4{0u, 0u, 0u, 0u};  // an all-zero block of a sum gives +0 codes
+      // Blocks whose amax is within 2^-16 of a power of two are quantized
+      // again from exact values, one at a time by the whole wave, after the
+      // packing above (so that y need not stay in registers along this path).
+      const bool near = near_pow2(amax);
+      const uint64_t nearm = __builtin_amdgcn_ballot_w64(near);
+      if (__builtin_expect(nearm != 0, 0)) {
+        for (uint64_t m = nearm; m; m &= m - 1) {
+          const int L = __builtin_ctzll(m);
+          exact_block<FRONT>(stage, L, lds_p[FRONT == FRONT_KRON ? wv : 0][L], lds_ia[FRONT == FRONT_KRON ? wv : 0][L],
+                             lane, lds_res[wv][L],
+                             STORE_Y ? lds_ys[STORE_Y ? wv : 0] : nullptr);
+          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          if constexpr (STORE_Y) {
+            if (lane == L) {
+#pragma unroll
+              for (int c = 0; c < 32; ++c) y[c] = lds_ys[wv][c];
+            }
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+          }
+        }
+        if (near) {
+          const unsigned* r = lds_res[wv][lane];
+          cw = u32x4{r[0], r[1], r[2], r[3]};
+          byte = r[4];
+        }
+      }
+    }
+    const auto rc = rsrc_uniform(a.codes + ub * 16, clamp_bytes(a.nblocks * 16 - ub * 16, kUnitCodes));
+    const auto rs = rsrc_uniform(a.scales + ub, clamp_bytes(a.nblocks - ub, kUnitBlocks));
+    __builtin_amdgcn_raw_buffer_store_b128(cw, rc, (uint32_t)(16 * lane), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)byte, rs, (uint32_t)lane, 0, 0);
+    if constexpr (STORE_Y) {
+      const auto ry = rsrc_uniform(a.Y + ub * 32, clamp_bytes((a.nblocks - ub) * 128, kUnitBlocks * 128));
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{y[4 * k], y[4 * k + 1], y[4 * k + 2],
+                                                                                 y[4 * k + 3]}),
+                                               ry, (uint32_t)(128 * lane + 16 * k), 0, 0);
+    }
+    ub += bstep;
+  };
+
+  // in unit order (the scheduler would otherwise be free to issue the second
+  // unit's loads first, and every wait for the first unit would then drain both)
+#pragma unroll
+  for (int s = 0; s < kDepth; ++s) {
+    load(s);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  for (int k0 = 0; k0 < n; k0 += kDepth) {
+#pragma unroll
+    for (int s = 0; s < kDepth; ++s)
+      if (k0 + s < n) compute(s);
+  }
+}
+
+template <int FRONT>
+const void* pick(bool store_y) {
+  return store_y ? (const void*)&flat_kernel<FRONT, true> : (const void*)&flat_kernel<FRONT, false>;
+}
+
+int gcd64(int nb) {
+  int g = 64;
+  while (nb % g) g >>= 1;
+  return g;
+}
+
+}  // namespace
+
+hipError_t launch_flat(int front, bool store_y, const FlatArgs& args, hipStream_t stream) {
+  const void* fn = nullptr;
+  switch (front) {
+    case FRONT_KRON: fn = pick<FRONT_KRON>(store_y); break;
+    case FRONT_PLAIN: fn = pick<FRONT_PLAIN>(store_y); break;
+    case FRONT_SMOOTH: fn = pick<FRONT_SMOOTH>(store_y); break;
+    case FRONT_HADAMARD: fn = pick<FRONT_HADAMARD>(store_y); break;
+    default: return hipErrorInvalidValue;
+  }
+  FlatArgs a = args;
+  a.nblocks = (int64_t)a.T * a.nb;
+  a.xbytes = a.nblocks * 64;
+  a.units = (a.nblocks + kUnitBlocks - 1) / kUnitBlocks;
+  a.phases = a.nb / gcd64(a.nb);
+  const int64_t per_phase = (a.units + a.phases - 1) / a.phases;
+  // one resident round of waves: every wave then owns about the same number of units
+  const int64_t slots = (int64_t)cu_count() * resident_per_cu(fn, 64 * kWaves) * kWaves;
+  int64_t chunks = a.req_waves > 0 ? (int64_t)a.req_waves / a.phases : slots / a.phases;
+  if (chunks > per_phase) chunks = per_phase;
+  if (chunks < 1) chunks = 1;
+  a.chunks = (int)chunks;
+  const int64_t waves = (int64_t)a.phases * a.chunks;
+  void* kargs[] = {&a};
+  return hipLaunchKernel(fn, dim3((unsigned)((waves + kWaves - 1) / kWaves)), dim3(64 * kWaves), kargs, 0, stream);
+}
+
+}  // namespace kq

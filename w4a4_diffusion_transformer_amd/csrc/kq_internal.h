@@ -60,6 +60,25 @@ struct QuadArgs {
   int ngroups, nchunks;
 };
 
+// Block-per-lane decomposition of the vector-ALU kernels: X as a flat
+// sequence of 64-byte blocks, a wave per unit of 64 consecutive blocks (one
+// per lane, staged through a wave-private LDS region), each wave visiting
+// units a whole number of rows apart so that each lane keeps one block
+// column.  Set by launch_flat: nblocks, xbytes, units, phases, chunks.
+struct FlatArgs {
+  const uint16_t* X;
+  int T, nb;
+  const float* P;
+  int pstride;
+  const float* m;  // channel multipliers (SmoothQuant front-end)
+  uint8_t* codes;
+  uint8_t* scales;
+  float* Y;
+  int64_t nblocks, xbytes, units;
+  int phases, chunks;
+  int req_waves = 0;  // requested total waves (tuning; 0: one resident round)
+};
+
 // Compute units of the current device (cached per device).
 int cu_count();
 // Workgroups of `fn` (block_threads threads, no dynamic LDS) resident per
@@ -72,6 +91,7 @@ int chunks_one_round(const void* fn, int block_threads, int ngroups, int ntiles,
 
 hipError_t launch_mfma(int ksrc, bool store_y, bool mod, const MfmaArgs& args, hipStream_t stream);
 hipError_t launch_quad(int front, bool store_y, const QuadArgs& args, hipStream_t stream);
+hipError_t launch_flat(int front, bool store_y, const FlatArgs& args, hipStream_t stream);
 // W4A4 GEMM: Y [M][N] = deq(A) deq(B)^T, A [M][K] and B [N][K] in MXFP4
 // (codes [rows][K/2], E8M0 scales [rows][K/32]); either output may be null.
 struct GemmArgs {

@@ -1,9 +1,4 @@
-// Vector-ALU front-ends fused with the MXFP4 quantizer (gfx950):
-//   FRONT_KRON      y = x K(j) as five fp32 2x2 butterfly stages, one per
-//                   Kronecker factor (K = G1 (x) ... (x) G5: multiplying a row
-//                   vector by it applies each G_k to the index bit it owns;
-//                   KroQuant's on-the-fly "15 scalars" kernel variant, Pith
-//                   review, "What carries the argument");
+// Vector-ALU comparison front-ends fused with the MXFP4 quantizer (gfx950):
 //   FRONT_PLAIN     y = x;
 //   FRONT_SMOOTH    y = x * m[c] (SmoothQuant per-channel scale);
 //   FRONT_HADAMARD  y = (x H_B)[c] / sqrt(B), fast Walsh-Hadamard butterflies
@@ -14,10 +9,10 @@
 // the fixed 16-byte piece l, i.e. channels 8q .. 8q+7 (q = l & 3) of block
 // l >> 2 of its column group, for every row it visits.  Loads (1 KB), code
 // stores (256 B) and scale stores (16 B) of a wave instruction are therefore
-// contiguous, and each lane keeps the coefficients of a single block in
-// registers.  Stages on channel bits 0-2 stay in registers; bits 3 and 4
-// pair lane l with l^1 and l^2 (the four lanes of a block), exchanged with
-// DPP quad permutes.  Rows stream with loads kept several rows ahead.
+// contiguous, and each lane keeps the multipliers of a single block in
+// registers.  Hadamard stages on channel bits 0-2 stay in registers; bits 3
+// and 4 pair lane l with l^1 and l^2 (the four lanes of a block), exchanged
+// with DPP quad permutes.  Rows stream with loads kept several rows ahead.
 #include "kq_device.hpp"
 #include "kq_internal.h"
 
@@ -28,59 +23,10 @@ namespace {
 constexpr int kWaves = 4;  // waves per workgroup, one row each per step
 constexpr int kDepth = 6;  // rows in flight per wave (current + 5 ahead)
 
-// Per-lane coefficients of one block for the butterfly front-end.
-struct Coef {
-  float g[3][4];  // G5, G4, G3 (channel bits 0, 1, 2): full 2x2, row-major
-  float cs[2];    // G2 (bit 3), G1 (bit 4): weight of this lane's own value
-  float cp[2];    //                          weight of the partner lane's value
-};
-
-__device__ __forceinline__ void set_full(float g[4], const Factor& f) {
-  g[0] = (float)f.g00;
-  g[1] = (float)f.g01;
-  g[2] = (float)f.g10;
-  g[3] = (float)f.g11;
-}
-
-// A cross-lane stage: this lane's channel has bit value beta for the factor:
-// y_own = x_own G[beta][beta] + x_partner G[1 - beta][beta].
-__device__ __forceinline__ void set_cross(float& cs, float& cp, const Factor& f, int beta) {
-  cs = (float)(beta ? f.g11 : f.g00);
-  cp = (float)(beta ? f.g01 : f.g10);
-}
-
-__device__ __forceinline__ void setup_coef(Coef& cf, const float* __restrict__ p15, int q, double* g_out) {
-  const Factors F = factors_f64(p15);
-  if (g_out) store_factors(F, g_out);  // for the exact path
-  set_full(cf.g[0], F.f5);             // channel bit 0
-  set_full(cf.g[1], F.f4);             // bit 1
-  set_full(cf.g[2], F.f3);             // bit 2
-  set_cross(cf.cs[0], cf.cp[0], F.f2, q & 1);   // bit 3: lanes l, l^1
-  set_cross(cf.cs[1], cf.cp[1], F.f1, q >> 1);  // bit 4: lanes l, l^2
-}
-
-// (v[i], v[i | bit]) <- (v[i], v[i | bit]) G for every pair differing in `bit`.
-template <int BIT>
-__device__ __forceinline__ void stage_in_reg(float v[8], const float g[4]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (i & BIT) continue;
-    const float x0 = v[i], x1 = v[i | BIT];
-    v[i] = fmaf(x1, g[2], x0 * g[0]);
-    v[i | BIT] = fmaf(x1, g[3], x0 * g[1]);
-  }
-}
-
 template <int XOR>
 __device__ __forceinline__ float partner(float v) {
   if constexpr (XOR == 1) return dpp_quad_xor1(v);
   else return dpp_quad_xor2(v);
-}
-
-template <int XOR>
-__device__ __forceinline__ void stage_cross(float v[8], float cs, float cp) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = fmaf(v[i], cs, partner<XOR>(v[i]) * cp);
 }
 
 // Walsh-Hadamard butterflies: (a, b) -> (a + b, a - b).
@@ -116,7 +62,6 @@ struct NoExact {
 
 template <int FRONT, bool STORE_Y>
 __global__ __launch_bounds__(64 * kWaves) void quad_kernel(QuadArgs a) {
-  __shared__ double lds_g[FRONT == FRONT_KRON ? 16 : 1][20];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -125,12 +70,7 @@ __global__ __launch_bounds__(64 * kWaves) void quad_kernel(QuadArgs a) {
   const bool live = j < a.nb;  // the last column group may be partial
   const int jc = live ? j : a.nb - 1;
 
-  Coef cf;
   float mult[8];
-  if constexpr (FRONT == FRONT_KRON) {
-    setup_coef(cf, a.P + (int64_t)jc * a.pstride, q, wv == 0 && q == 0 ? lds_g[lane >> 2] : nullptr);
-    __syncthreads();
-  }
   if constexpr (FRONT == FRONT_SMOOTH) {
     const f32x4* mp = reinterpret_cast<const f32x4*>(a.m + 32 * jc + 8 * q);
     const f32x4 m0 = mp[0], m1 = mp[1];
@@ -179,13 +119,7 @@ __global__ __launch_bounds__(64 * kWaves) void quad_kernel(QuadArgs a) {
     const bool in = cleft > 0;
     float y[8];
     unpack8(b, y);
-    if constexpr (FRONT == FRONT_KRON) {
-      stage_in_reg<1>(y, cf.g[0]);
-      stage_in_reg<2>(y, cf.g[1]);
-      stage_in_reg<4>(y, cf.g[2]);
-      stage_cross<1>(y, cf.cs[0], cf.cp[0]);
-      stage_cross<2>(y, cf.cs[1], cf.cp[1]);
-    } else if constexpr (FRONT == FRONT_SMOOTH) {
+    if constexpr (FRONT == FRONT_SMOOTH) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) y[i] *= mult[i];
     } else if constexpr (FRONT == FRONT_HADAMARD) {
@@ -208,9 +142,7 @@ __global__ __launch_bounds__(64 * kWaves) void quad_kernel(QuadArgs a) {
     // rows past the end hold zeros (amax 0): the exact path never runs for them
     const uint16_t* xblk = (in ? cx : a.X) + 32 * jc;
     unsigned word, byte;
-    if constexpr (FRONT == FRONT_KRON) {
-      mx_epilogue<LAYOUT_QUAD, true>(y, xblk, q, ExactFromFactors{lds_g[lane >> 2]}, word, byte);
-    } else if constexpr (FRONT == FRONT_HADAMARD) {
+    if constexpr (FRONT == FRONT_HADAMARD) {
       const int hb = 1 << a.hlog;
       const int off = (32 * jc) & (hb - 1);
       mx_epilogue<LAYOUT_QUAD, true>(y, xblk, q, ExactHadamardB{xblk - off, hb, off}, word, byte);
@@ -257,7 +189,6 @@ const void* pick(bool store_y) {
 hipError_t launch_quad(int front, bool store_y, const QuadArgs& args, hipStream_t stream) {
   const void* fn = nullptr;
   switch (front) {
-    case FRONT_KRON: fn = pick<FRONT_KRON>(store_y); break;
     case FRONT_PLAIN: fn = pick<FRONT_PLAIN>(store_y); break;
     case FRONT_SMOOTH: fn = pick<FRONT_SMOOTH>(store_y); break;
     case FRONT_HADAMARD: fn = pick<FRONT_HADAMARD>(store_y); break;
