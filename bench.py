@@ -7,9 +7,12 @@ from the 256 MB Infinity Cache.  Throughput counts the algorithmic bytes of
 the path, 2 B in + 0.5 B codes + 1/32 B scales per element (parameters, 23 KB
 per call, excluded).  Inputs are resident in HBM before timing starts.
 
-Prints one JSON line (rank 0).  Also reported in the same line: the three
-comparison kernels and the other two KroQuant variants on the same inputs,
-the roofline position of the dominant kernel, and the CPU oracle's rate.
+Prints one JSON line (rank 0).  Also reported in the same line: the other
+KroQuant variants and the three comparison kernels on the same inputs, the
+stream probe (the same traffic with no arithmetic: the ceiling of this access
+pattern) with every kernel's share of it, the roofline position of the
+dominant kernel, the CPU oracle's rate on every matrix (one thread and all
+cores), and per-shape tables (median, min and max over repetitions).
 """
 from __future__ import annotations
 
@@ -27,7 +30,9 @@ METRIC = "transform+MXFP4 quantize GB/s and % of MI355X HBM peak; Gelem/s per sh
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD public specification
 BYTES_PER_ELEM = 2.0 + 0.5 + 1.0 / 32.0
 CALLS = 57
-KERNEL_SOURCES = ["kq_device.hpp", "kq_mfma.hip"]  # the dominant kernel (mfma_kernel) and its device helpers
+ROUNDS = 7  # timed rounds per per-shape entry: median, min and max are over these
+# sources of the default kernel (the block-per-lane butterfly) and its device helpers
+KERNEL_SOURCES = ["kq_device.hpp", "kq_flat.hip"]
 
 
 def kernel_source_hash() -> str:
@@ -38,26 +43,77 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+def load_profile(kernel: str, workload: str) -> dict:
+    """HBM bytes per launch (rocprofv3 counters) and the kernel-trace average of
+    the committed summaries, if they were taken on the current kernel sources."""
+    out = {}
+    for key, fname in (("traffic_bytes_per_launch", f"traffic_{kernel}_{workload}.json"),
+                       ("trace_avg_kernel_us", f"trace_{kernel}_{workload}.json")):
+        try:
+            with open(os.path.join(ROOT, "profiles", fname)) as f:
+                t = json.load(f)
+        except (OSError, ValueError):
+            continue
+        if t.get("kernel_source_hash") == kernel_source_hash():
+            out[key] = t.get(key)
+    return out
+
+
+def cpu_info() -> dict:
+    model = None
     try:
-        with open(path) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if t.get("kernel_source_hash") != kernel_source_hash():
-        return None
-    return t.get("traffic_bytes_per_launch")
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model}
+
+
+def time_calls(torch, fn, argv, reps, rounds=ROUNDS):
+    """Per-call seconds over `rounds` timed rounds of `reps` back-to-back calls
+    (argv cycled), after >= 100 ms of warm-up calls: MI355X clocks drop while
+    the GPU idles during input generation and take a while to come back."""
+    n = len(argv)
+    t_warm = time.perf_counter() + 0.1
+    while time.perf_counter() < t_warm:
+        for i in range(reps):
+            assert fn(*argv[i % n]) == 0
+        torch.cuda.synchronize()
+    out = []
+    for _ in range(rounds):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            fn(*argv[i % n])
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) * 1e-3 / reps)
+    return sorted(out)
+
+
+def rate_entry(nbytes, nelem, secs, probe_sec=None):
+    med = secs[len(secs) // 2]
+    e = {"GBps": round(nbytes / med / 1e9, 1), "Gelem_s": round(nelem / med / 1e9, 1),
+         "pct_peak": round(100 * nbytes / med / 1e9 / HBM_PEAK_GBS, 1), "us": round(med * 1e6, 2),
+         "us_min": round(secs[0] * 1e6, 2), "us_max": round(secs[-1] * 1e6, 2)}
+    if probe_sec:
+        e["pct_of_probe"] = round(100 * probe_sec / med, 1)
+    return e
 
 
 def shape_table(kq, torch, np, synth, dev):
-    """GB/s and Gelem/s of every kernel on every matrix of the PixArt, SANA and FLUX workloads.
+    """Every kernel on every matrix of the PixArt, SANA and FLUX workloads.
 
     Each matrix is copied enough times that one pass over the copies (inputs
     and outputs) exceeds 512 MB, twice the Infinity Cache, and calls cycle
-    through the copies back to back on one stream."""
+    through the copies back to back on one stream; per call: the median,
+    minimum and maximum over ROUNDS timed rounds.  The stream probe's time on
+    the same copies gives each kernel's share of the access pattern's
+    ceiling."""
     out = {}
     # plus the shard one GPU of an 8-way tensor-parallel FLUX.1-schnell MLP fc2 input would hold
     # (X2's 12288 channels split in eight 32-aligned slices: 4608 x 1536), same distribution as X2
@@ -78,58 +134,81 @@ def shape_table(kq, torch, np, synth, dev):
         Kbf = torch.empty((P.shape[0], 3, 32, 32), dtype=torch.int16, device=dev)
         kq.kq_build_blocks(Pd, P.shape[0], None, Kbf, 3)
         # Calls go straight to the C ABI with pointers marshalled once: these kernels run
-        # 10-40 us, so per-call host overhead must stay well below that for back-to-back
-        # launches on the stream (HIP graph replay was measured to add ~9 us per kernel).
+        # 6-40 us, so per-call host overhead must stay well below that for back-to-back
+        # launches on the stream.
         L = kq.lib()
         stream = torch.cuda.current_stream().cuda_stream
         xs = [x.data_ptr() for x in Xs]
         os_ = [(c_.data_ptr(), s_.data_ptr()) for c_, s_ in outs]
         pp, mp, kp = Pd.data_ptr(), md.data_ptr(), Kbf.data_ptr()
         calls = {
+            "stream_probe": (L.kq_stream_probe, lambda i: (xs[i], T, d, *os_[i], stream)),
             "kroquant": (L.kq_quantize_ex, lambda i: (xs[i], T, d, pp, pstride, None, kq.KQ_AUTO, *os_[i], stream)),
+            "kroquant_mfma_otf": (L.kq_quantize_ex,
+                                  lambda i: (xs[i], T, d, pp, pstride, None, kq.KQ_MFMA_OTF, *os_[i], stream)),
             "kroquant_mfma_dense": (L.kq_quantize_ex,
                                     lambda i: (xs[i], T, d, None, pstride, kp, kq.KQ_MFMA_DENSE, *os_[i], stream)),
-            "kroquant_butterfly": (L.kq_quantize_ex,
-                                   lambda i: (xs[i], T, d, pp, pstride, None, kq.KQ_BUTTERFLY, *os_[i], stream)),
         }
         if not spec.shared_k:
             calls["smoothquant"] = (L.kq_smooth_quantize, lambda i: (xs[i], T, d, mp, *os_[i], stream))
             calls["plain"] = (L.kq_mx_quantize, lambda i: (xs[i], T, d, *os_[i], stream))
             calls["hadamard32"] = (L.kq_hadamard_quantize, lambda i: (xs[i], T, d, *os_[i], stream))
-        row = {"T": T, "d": d}
+        row = {"T": T, "d": d, "auto_variant": kq.variant_name(kq.kq_auto_variant(T, d, True, False))}
         if not spec.shared_k:
-            # kq_tune's pick for this shape (K_params and the dense split both supplied; kq_tune takes
-            # per-block parameters only), then timed through KQ_AUTO
+            # kq_tune's record for this shape (K_params and the dense split both supplied), then
+            # timed through KQ_AUTO on the cold copies
             tuned = kq.kq_tune(Xs[0], Pd, Kbf, *outs[0], reps=30)
             row["tuned_variant"] = kq.variant_name(tuned)
             calls["kroquant_tuned"] = (L.kq_quantize_ex,
                                        lambda i: (xs[i], T, d, pp, 15, kp, kq.KQ_AUTO, *os_[i], stream))
+        probe = None
         for name, (fn, mk) in calls.items():
             argv = [mk(i) for i in range(copies)]
-            reps = max(60, 4 * copies)
-            # warm-up of at least 100 ms of back-to-back calls: clocks drop while the GPU
-            # idles (input generation runs on the host), and they take a while to come back
-            t_warm = time.perf_counter() + 0.1
-            while time.perf_counter() < t_warm:
-                for i in range(reps):
-                    assert fn(*argv[i % copies]) == 0
-                torch.cuda.synchronize()
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
-            for i in range(reps):
-                fn(*argv[i % copies])
-            b.record()
-            torch.cuda.synchronize()
-            sec = a.elapsed_time(b) * 1e-3 / reps
-            row[name] = {"GBps": round(nbytes / sec / 1e9, 1), "Gelem_s": round(T * d / sec / 1e9, 1),
-                         "pct_peak": round(100 * nbytes / sec / 1e9 / HBM_PEAK_GBS, 1), "us": round(sec * 1e6, 2)}
+            secs = time_calls(torch, fn, argv, max(60, 4 * copies))
+            if name == "stream_probe":
+                probe = secs[len(secs) // 2]
+            row[name] = rate_entry(nbytes, T * d, secs, probe)
+        if "smoothquant" in row:
+            row["kroquant_time_over_smoothquant_time"] = round(row["kroquant"]["us"] / row["smoothquant"]["us"], 3)
         out[spec.name] = row
         kq.kq_tune_reset()
         del Xs, outs
         print(f"# {spec.name}: " + ", ".join(f"{k} {v['GBps']}" for k, v in row.items() if isinstance(v, dict)),
               file=sys.stderr, flush=True)
     return out
+
+
+def cpu_baseline(oracle, synth, X_stress, P_stress):
+    """The oracle as it stands (plain single-threaded C, fp64) on the GPU machine's
+    host cores: one full call per matrix of the PixArt, SANA and FLUX workloads
+    and one of the stress matrix, on one thread and with the rows split across
+    all the threads this box's share allows (the same C routine per thread)."""
+    info = cpu_info()
+    threads = max(1, min(16, os.cpu_count() or 1))
+    per = {}
+    total = {1: [0.0, 0.0], threads: [0.0, 0.0]}  # bytes, seconds
+    mats = [(s.name, synth.matrix(s), synth.params(s), 0 if s.shared_k else 15)
+            for c in (1, 2, 3) for s in synth.CONFIGS[c]]
+    mats.append(("stress", X_stress, P_stress, 15))
+    for name, X, P, pstride in mats:
+        nbytes = BYTES_PER_ELEM * X.size
+        e = {}
+        for th in sorted(total):
+            t0 = time.perf_counter()
+            oracle.quantize_rows(oracle.KRON, X, P, pstride, threads=th)
+            dt = time.perf_counter() - t0
+            e[f"GBps_{th}_threads"] = round(nbytes / dt / 1e9, 4)
+            total[th][0] += nbytes
+            total[th][1] += dt
+        per[name] = e
+        print(f"# cpu oracle {name}: {e}", file=sys.stderr, flush=True)
+    v = total[threads][0] / total[threads][1] / 1e9
+    return {"value": round(v, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": (f"one full kq_quantize-equivalent call on each of the 8 matrices (PixArt, SANA, FLUX and "
+                       f"stress), rows split over {threads} threads; {total[threads][1]:.1f} s on {threads} threads, "
+                       f"{total[1][1]:.1f} s on one"),
+            "single_thread_GBps": round(total[1][0] / total[1][1] / 1e9, 4),
+            "nproc": info["nproc"], "cpu_model": info["cpu_model"], "per_matrix": per}
 
 
 def adaln_table(kq, torch, np, synth, dev):
@@ -181,21 +260,9 @@ def adaln_table(kq, torch, np, synth, dev):
 
         row = {"T": T, "d": d, "tokens_per_sample": tps}
         for label, fn in (("fused_quantize_adaln", fused), ("row_stats", stats), ("unfused_torch_eager_modulate_then_quantize", unfused)):
-            reps = max(60, 4 * copies)
-            t_warm = time.perf_counter() + 0.1
-            while time.perf_counter() < t_warm:
-                for i in range(reps):
-                    assert fn(i % copies) == 0
-                torch.cuda.synchronize()
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record()
-            for i in range(reps):
-                fn(i % copies)
-            b.record()
-            torch.cuda.synchronize()
-            sec = a.elapsed_time(b) * 1e-3 / reps
-            row[label] = {"us": round(sec * 1e6, 2)}
+            secs = time_calls(torch, fn, [(i,) for i in range(copies)], max(60, 4 * copies))
+            sec = secs[len(secs) // 2]
+            row[label] = {"us": round(sec * 1e6, 2), "us_min": round(secs[0] * 1e6, 2), "us_max": round(secs[-1] * 1e6, 2)}
             if label == "fused_quantize_adaln":
                 fb = nbytes + 8 * T
                 row[label].update({"GBps": round(fb / sec / 1e9, 1), "pct_peak": round(100 * fb / sec / 1e9 / HBM_PEAK_GBS, 1)})
@@ -282,7 +349,9 @@ def bf16_matmul(torch, dev, M, N, K, kq_sec):
 
 
 def library_mxfp4(torch, a, asc, b, bsc, y, M, N, K, kq_sec):
-    """hipBLASLt's MXFP4 GEMM (torch._scaled_mm) on the same operands; None if unavailable."""
+    """hipBLASLt's MXFP4 GEMM (torch._scaled_mm) on the same operands; None if this torch build lacks
+    the FP4 types, {"us": None, "error": ...} if the library call fails or one call takes more than 20
+    times this kernel's time (not retried, not timed)."""
     f4, e8 = getattr(torch, "float4_e2m1fn_x2", None), getattr(torch, "float8_e8m0fnu", None)
     if f4 is None or e8 is None:
         return None
@@ -292,34 +361,24 @@ def library_mxfp4(torch, a, asc, b, bsc, y, M, N, K, kq_sec):
                                 out_dtype=torch.bfloat16)
 
     try:
-        yl = None
-        for _ in range(2):  # the first call can fail while the library's kernel generator initialises
-            try:
-                yl = call()
-                torch.cuda.synchronize()
-                break
-            except RuntimeError:
-                yl = None
-        if yl is None:
-            return None
+        yl = call()
+        torch.cuda.synchronize()
         # bf16 steps between the two outputs (order-preserving integer map of the bf16 bit patterns)
         def key(t):
             i = t.view(torch.int16).to(torch.int32)
             return torch.where(i < 0, -32768 - i, i)
         steps = int((key(yl) - key(y)).abs().max().item())
-        # one timed call first: where the library takes far longer than this kernel (it took
-        # seconds per call at K = 1152 on MI355X), that single call is the figure reported
+        # one call first: where the library takes far longer than this kernel (seconds per call
+        # at some shapes on MI355X), the shape is not timed and no figure is reported for it
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
         call()
         e1.record()
         torch.cuda.synchronize()
-        one = e0.elapsed_time(e1) * 1e-3
-        if one > 20 * kq_sec:
-            return {"us": round(one * 1e6, 1), "TFLOPs": round(2.0 * M * N * K / one / 1e12, 1),
-                    "kq_time_over_library_time": round(kq_sec / one, 4), "max_bf16_steps_apart": steps,
-                    "reps": 1}
+        if e0.elapsed_time(e1) * 1e-3 > 20 * kq_sec:
+            return {"us": None, "max_bf16_steps_apart": steps,
+                    "error": "one call took more than 20 times this kernel's time; not timed"}
         t_warm = time.perf_counter() + 0.1
         while time.perf_counter() < t_warm:
             call()
@@ -337,8 +396,9 @@ def library_mxfp4(torch, a, asc, b, bsc, y, M, N, K, kq_sec):
                 "kq_time_over_library_time": round(kq_sec / sec, 3), "max_bf16_steps_apart": steps,
                 "reps": reps}
     except RuntimeError as e:
-        print(f"# hipBLASLt MXFP4 unavailable: {str(e)[:120]}", file=sys.stderr, flush=True)
-        return None
+        # the library's failure is recorded as it is; this shape is not called again
+        print(f"# hipBLASLt MXFP4 failed at {M}x{N}x{K}: {str(e)[:160]}", file=sys.stderr, flush=True)
+        return {"us": None, "error": str(e)[:300]}
 
 
 def parse():
@@ -402,17 +462,18 @@ def main():
             call(i)
 
     def timed(call, steps, warmup):
+        """(total ms over `steps` steps, sorted per-step ms): events around every step on the launch stream."""
         for _ in range(warmup):
             step(call)
         torch.cuda.synchronize()
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        s.record()
-        for _ in range(steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record()
+        for k in range(steps):
             step(call)
-        e.record()
+            ev[k + 1].record()
         torch.cuda.synchronize()
-        return s.elapsed_time(e)  # ms
+        per = sorted(ev[k].elapsed_time(ev[k + 1]) for k in range(steps))
+        return ev[0].elapsed_time(ev[-1]), per
 
     main_v = kq.VARIANTS[args.variant]
     if args.profile_pass:
@@ -420,9 +481,20 @@ def main():
             kron(main_v)(0)
         for v in (kq.KQ_MFMA_DENSE, kq.KQ_MFMA_OTF, kq.KQ_BUTTERFLY):
             kron(v)(1)
+        kq.kq_stream_probe(Xs[0], *outs[0])
         kq.kq_smooth_quantize(Xs[0], md, *outs[0])
         kq.kq_mx_quantize(Xs[0], *outs[0])
         kq.kq_hadamard_quantize(Xs[0], *outs[0])
+        # the FLUX matrices once each with the default kernel and the SmoothQuant kernel
+        for fs in synth.CONFIGS[3]:
+            fx = torch.from_numpy(synth.matrix(fs).view(np.int16)).to(dev)
+            fp = torch.from_numpy(synth.params(fs)).to(dev)
+            fo = kq.alloc_outputs(fx)
+            fm = torch.ones(fs.d, dtype=torch.float32, device=dev)
+            kq.kq_quantize(fx, fp, *fo)
+            kq.kq_smooth_quantize(fx, fm, *fo)
+            kq.kq_quantize_ex(fx, fp, 15, None, kq.KQ_MFMA_OTF, *fo)
+            del fx, fo
         # the W4A4 GEMM once at the FLUX MLP fc1 shape
         gm, gn, gk = 4608, 12288, 3072
         ga = torch.randint(0, 256, (gm, gk // 2), dtype=torch.uint8, device=dev)
@@ -440,46 +512,39 @@ def main():
         print(json.dumps({"profile_pass": True, "copy_bytes": a.numel() * 2}))
         return
 
-    ms = timed(kron(main_v), args.steps, args.warmup)
+    ms, per_step = timed(kron(main_v), args.steps, args.warmup)
     ms_step = ms / args.steps
     bytes_call = BYTES_PER_ELEM * n
     gbs = bytes_call * CALLS * args.steps / (ms * 1e-3) / 1e9
     launch_us = ms * 1e3 / (args.steps * CALLS)
+    print(f"# stress: {gbs:.1f} GB/s, {launch_us:.2f} us per launch", file=sys.stderr, flush=True)
+
+    def leg(call, steps):
+        t, per = timed(call, steps, 2)
+        return {"GBps": round(bytes_call * CALLS * steps / (t * 1e-3) / 1e9, 1),
+                "us": round(t * 1e3 / (steps * CALLS), 2),
+                "us_min": round(per[0] * 1e3 / CALLS, 2), "us_max": round(per[-1] * 1e3 / CALLS, 2)}
 
     comparison = {}
     if not args.no_compare:
-        def rate(call):
-            t = timed(call, max(2, args.steps // 2), 1)
-            return round(bytes_call * CALLS * max(2, args.steps // 2) / (t * 1e-3) / 1e9, 1)
-
+        k = max(5, args.steps // 2)
+        comparison["stream_probe"] = leg(lambda i: kq.kq_stream_probe(Xs[i & 1], *outs[i & 1]), k)
         for name, v in (("mfma_dense", kq.KQ_MFMA_DENSE), ("mfma_otf", kq.KQ_MFMA_OTF),
                         ("butterfly", kq.KQ_BUTTERFLY)):
-            comparison[f"kroquant_{name}_GBps"] = rate(kron(v))
-        comparison["smoothquant_mxfp4_GBps"] = rate(lambda i: kq.kq_smooth_quantize(Xs[i & 1], md, *outs[i & 1]))
-        comparison["plain_mxfp4_GBps"] = rate(lambda i: kq.kq_mx_quantize(Xs[i & 1], *outs[i & 1]))
-        comparison["hadamard32_mxfp4_GBps"] = rate(lambda i: kq.kq_hadamard_quantize(Xs[i & 1], *outs[i & 1]))
+            comparison[f"kroquant_{name}"] = leg(kron(v), k)
+        comparison["smoothquant_mxfp4"] = leg(lambda i: kq.kq_smooth_quantize(Xs[i & 1], md, *outs[i & 1]), k)
+        comparison["plain_mxfp4"] = leg(lambda i: kq.kq_mx_quantize(Xs[i & 1], *outs[i & 1]), k)
+        comparison["hadamard32_mxfp4"] = leg(lambda i: kq.kq_hadamard_quantize(Xs[i & 1], *outs[i & 1]), k)
         for hb in (64, 128, 256, 512):
-            comparison[f"hadamard{hb}_mxfp4_GBps"] = rate(
-                lambda i, hb=hb: kq.kq_hadamard_quantize_ex(Xs[i & 1], hb, *outs[i & 1]))
-        comparison["kroquant_time_over_smoothquant_time"] = round(comparison["smoothquant_mxfp4_GBps"] / gbs, 4)
+            comparison[f"hadamard{hb}_mxfp4"] = leg(
+                lambda i, hb=hb: kq.kq_hadamard_quantize_ex(Xs[i & 1], hb, *outs[i & 1]), k)
+        probe_us = comparison["stream_probe"]["us"]
+        for v in comparison.values():
+            v["pct_of_probe"] = round(100 * probe_us / v["us"], 1)
+        comparison["kroquant_time_over_smoothquant_time"] = round(launch_us / comparison["smoothquant_mxfp4"]["us"], 4)
+        comparison["kroquant_pct_of_probe"] = round(100 * probe_us / launch_us, 1)
         comparison["pages_context"] = ("KroQuant quantizer up to 14% faster than the SmoothQuant kernel on an MI350 "
                                        "(Triton); another machine, context only")
-
-    cpu = None
-    if not args.no_cpu:
-        import oracle
-
-        # the oracle as it stands, single-threaded, on whole calls of this workload until ~10 s have passed
-        t1 = time.perf_counter()
-        calls = 0
-        while True:
-            oracle.quantize_rows(oracle.KRON, X, P, threads=1)
-            calls += 1
-            dt = time.perf_counter() - t1
-            if dt >= 10.0 or calls >= 3:
-                break
-        cpu = {"value": round(bytes_call * calls / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": f"{calls} full call(s) of the stress workload ({T} x {d}), single thread, {dt:.1f} s"}
 
     per_shape = None
     if not args.no_shapes:
@@ -490,14 +555,25 @@ def main():
     gemm = None
     if not args.no_gemm:
         gemm = gemm_table(kq, torch, np, dev)
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+
+        cpu = cpu_baseline(oracle, synth, X, P)
 
     variant_name = args.variant
     kernel = kq.variant_name(kq.kq_auto_variant(T, d, True, False)) if variant_name == "auto" else variant_name
-    traffic = load_traffic(kernel, "stress")
-    roofline = {"bound": "hbm", "achieved": round(bytes_call / (launch_us * 1e-6) / 1e9, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(bytes_call / (launch_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "kernel": f"kq {kernel}", "avg_launch_us": round(launch_us, 2),
+    prof = load_profile(kernel, "stress")
+    achieved = bytes_call / (launch_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": prof.get("traffic_bytes_per_launch"),
+                "kernel": f"kq {kernel}", "avg_launch_us": round(launch_us, 2),
+                "step_ms_median": round(per_step[len(per_step) // 2], 4), "step_ms_min": round(per_step[0], 4),
+                "step_ms_max": round(per_step[-1], 4),
                 "algorithmic_bytes_per_launch": int(bytes_call)}
+    if prof.get("trace_avg_kernel_us"):
+        roofline["trace_avg_kernel_us"] = prof["trace_avg_kernel_us"]
+        roofline["frac_from_trace"] = round(bytes_call / (prof["trace_avg_kernel_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
 
     out = {
         "metric": METRIC,
@@ -510,7 +586,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"stress: X[{T} x {d}] bf16 Student-t(3), 1% outlier channels x200, 1% zero blocks; "
                                f"{CALLS} back-to-back kq_quantize calls per step",

@@ -105,7 +105,7 @@ typedef enum {
 typedef enum { KQ_FRONT_KRON = 0, KQ_FRONT_PLAIN = 1, KQ_FRONT_SMOOTH = 2, KQ_FRONT_HADAMARD = 3 } kq_front;
 
 /* ABI version of this header (bumped on any signature or layout change). */
-#define KQ_ABI_VERSION 5
+#define KQ_ABI_VERSION 6
 int kq_abi_version(void);
 
 /* Static, never-NULL description of a status code. */
@@ -284,7 +284,8 @@ kq_status kq_row_stats(const uint16_t* X, int64_t tokens, int64_t d, float eps, 
  * with the same inputs as kq_quantize_ex; KQ_BUTTERFLY -> KQ_ERR_VARIANT
  * (KQ_AUTO never resolves to it here: where KQ_VARIANT or a kq_tune record
  * names the butterfly, this entry point takes KQ_MFMA_OTF).
- * row_stats must be 8-byte aligned, mod_scale / mod_shift 4-byte aligned.
+ * row_stats must be 8-byte aligned, mod_scale / mod_shift 16-byte aligned
+ * (KQ_ERR_ALIGN otherwise).
  */
 kq_status kq_quantize_adaln(const uint16_t* X, int64_t tokens, int64_t d, const float* row_stats,
                             const float* mod_scale, const float* mod_shift, int64_t tokens_per_sample,
@@ -319,6 +320,20 @@ kq_status kq_build_blocks_inverse_t(const float* K_params, int64_t nb, float* K_
 kq_status kq_gemm_mx(const uint8_t* A_codes, const uint8_t* A_scales, int64_t M, const uint8_t* B_codes,
                      const uint8_t* B_scales, int64_t N, int64_t K, float* Y_f32, uint16_t* Y_bf16,
                      hipStream_t stream);
+
+/*
+ * Measurement entry (not a quantizer): moves exactly the traffic of
+ * kq_quantize's default kernel on X [tokens][d] (every bf16 of X read once in
+ * 4 KB units of 64 consecutive 32-channel blocks, one 16-byte record per
+ * block written to out_codes [tokens][d/2] and one byte per block to
+ * out_scales [tokens][d/32], the same grid and unit order) with no arithmetic:
+ * the outputs hold an XOR digest of the input, not codes.  Its rate is the
+ * ceiling this access pattern reaches on the device, against which the
+ * quantizers' rates are reported (the Pith review's Fig. 3 reports the
+ * quantizer's effective HBM bandwidth).  Errors as kq_mx_quantize.
+ */
+kq_status kq_stream_probe(const uint16_t* X, int64_t tokens, int64_t d, uint8_t* out_codes, uint8_t* out_scales,
+                          hipStream_t stream);
 
 #ifdef __cplusplus
 }

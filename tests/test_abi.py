@@ -150,6 +150,20 @@ def test_row_stats_argument_checks(lib):
     assert lib.kq_row_stats(A, 4, 64, 1e-6, None, None) == KQ_ERR_NULL
     assert lib.kq_row_stats(A + 2, 4, 64, 1e-6, B, None) == KQ_ERR_ALIGN
     assert lib.kq_row_stats(A, 4, 64, 1e-6, B + 4, None) == KQ_ERR_ALIGN
+
+
+def test_stream_probe_argument_checks(lib):
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.kq_stream_probe.argtypes = [vp, i64, i64, vp, vp, vp]
+    p = lib.kq_stream_probe
+    assert p(A, 4, 48, C, D, None) == KQ_ERR_SHAPE
+    assert p(A, -1, 64, C, D, None) == KQ_ERR_SHAPE
+    assert p(None, 4, 64, C, D, None) == KQ_ERR_NULL
+    assert p(A, 4, 64, C, None, None) == KQ_ERR_NULL
+    assert p(A + 2, 4, 64, C, D, None) == KQ_ERR_ALIGN
+    assert p(A, 4, 64, C + 8, D, None) == KQ_ERR_ALIGN
+    assert p(A, 4, 64, A + 16, D, None) == KQ_ERR_ALIAS
+    assert p(A, 0, 64, None, None, None) == KQ_OK
     assert lib.kq_row_stats(A, 4, 64, 1e-6, A + 8, None) == KQ_ERR_ALIAS
 
 
@@ -167,6 +181,9 @@ def test_quantize_adaln_argument_checks(lib):
     assert q(None, 100, 64, B, C, D, 64, E, 15, None, 0, F, G, None) == KQ_ERR_NULL
     assert q(A, 100, 64, B + 4, C, D, 64, E, 15, None, 0, F, G, None) == KQ_ERR_ALIGN
     assert q(A, 100, 64, B, C + 2, D, 64, E, 15, None, 0, F, G, None) == KQ_ERR_ALIGN
+    # the modulation vectors are read 16 bytes at a time
+    assert q(A, 100, 64, B, C + 4, D, 64, E, 15, None, 0, F, G, None) == KQ_ERR_ALIGN
+    assert q(A, 100, 64, B, C, D + 8, 64, E, 15, None, 0, F, G, None) == KQ_ERR_ALIGN
     # an output overlapping the statistics or a modulation vector
     assert q(A, 100, 64, B, C, D, 64, E, 15, None, 0, B + 64, G, None) == KQ_ERR_ALIAS
     assert q(A, 100, 64, B, C, D, 64, E, 15, None, 0, F, D + 16, None) == KQ_ERR_ALIAS

@@ -174,6 +174,32 @@ def test_fused_full_workloads(name, T, d, tps, kind):
     check(f"adaln {name}", X, P, st, sc, sh, tps, kq.KQ_MFMA_OTF)
 
 
+def test_modulation_vectors_at_an_offset():
+    """Modulation vectors passed as views 16 bytes into larger buffers (the
+    alignment the entry point requires) give the same bytes as contiguous ones;
+    a view 4 bytes in is refused (KQ_ERR_ALIGN)."""
+    T, d, tps = 128, 1152, 64
+    X, P, st, sc, sh = inputs(T, d, tps, seed=77)
+    codes, scales = run_fused(X, P, st, sc, sh, tps, kq.KQ_MFMA_OTF)
+    big_sc = torch.zeros(sc.size + 4, dtype=torch.float32, device="cuda:0")
+    big_sh = torch.zeros(sh.size + 4, dtype=torch.float32, device="cuda:0")
+    big_sc[4:] = dev(sc).reshape(-1)
+    big_sh[4:] = dev(sh).reshape(-1)
+    Xd, std, Pd = dev(X), dev(st), dev(P)  # held for the duration of the calls
+    c2, s2 = kq.alloc_outputs(Xd)
+    L = kq.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    args = lambda off_sc, off_sh: (Xd.data_ptr(), T, d, std.data_ptr(), big_sc.data_ptr() + off_sc,
+                                   big_sh.data_ptr() + off_sh, tps, Pd.data_ptr(), 15, None, kq.KQ_MFMA_OTF,
+                                   c2.data_ptr(), s2.data_ptr(), stream)
+    assert L.kq_quantize_adaln(*args(16, 16)) == 0
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(c2), codes)
+    np.testing.assert_array_equal(host(s2), scales)
+    assert L.kq_quantize_adaln(*args(12, 16)) == 3
+    assert L.kq_quantize_adaln(*args(16, 4)) == 3
+
+
 def test_fused_error_codes():
     X, P, st, sc, sh = inputs(100, 64, 64, seed=9)
     Xd = dev(X)

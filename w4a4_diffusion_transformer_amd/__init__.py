@@ -21,7 +21,7 @@ __all__ = [
     "kq_mx_quantize", "kq_smooth_quantize", "kq_hadamard_quantize", "kq_transform_f32",
     "alloc_outputs", "LIB_PATH", "kq_auto_variant", "variant_name", "kq_row_stats", "kq_quantize_adaln",
     "kq_build_blocks_inverse_t", "kq_gemm_mx", "kq_hadamard_quantize_ex", "kq_build_blocks16", "kq_tune",
-    "kq_tune_reset",
+    "kq_tune_reset", "kq_stream_probe",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkq.so")
@@ -55,6 +55,7 @@ def lib() -> ctypes.CDLL:
         L.kq_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp]
         L.kq_quantize_ex.argtypes = [vp, i64, i64, vp, i64, vp, ci, vp, vp, vp]
         L.kq_mx_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.kq_stream_probe.argtypes = [vp, i64, i64, vp, vp, vp]
         L.kq_smooth_quantize.argtypes = [vp, i64, i64, vp, vp, vp, vp]
         L.kq_hadamard_quantize.argtypes = [vp, i64, i64, vp, vp, vp]
         L.kq_transform_f32.argtypes = [ci, vp, i64, i64, vp, i64, vp, ci, vp, vp, vp, vp, vp]
@@ -69,7 +70,8 @@ def lib() -> ctypes.CDLL:
         L.kq_tune_reset.argtypes = []
         L.kq_tune_reset.restype = None
         L.kq_quantize_adaln.argtypes = [vp, i64, i64, vp, vp, vp, i64, vp, i64, vp, ci, vp, vp, vp]
-        for name in ("kq_build_blocks", "kq_quantize", "kq_quantize_ex", "kq_mx_quantize", "kq_smooth_quantize",
+        for name in ("kq_build_blocks", "kq_quantize", "kq_quantize_ex", "kq_mx_quantize", "kq_stream_probe",
+                     "kq_smooth_quantize",
                      "kq_hadamard_quantize", "kq_transform_f32", "kq_row_stats", "kq_quantize_adaln",
                      "kq_build_blocks_inverse_t", "kq_gemm_mx", "kq_hadamard_quantize_ex", "kq_build_blocks16", "kq_tune"):
             getattr(L, name).restype = ci
@@ -169,6 +171,14 @@ def kq_mx_quantize(X, out_codes, out_scales, stream=None):
     T, d = _shape(X)
     _check(lib().kq_mx_quantize(_ptr(X, "X", _BF16), T, d, _ptr(out_codes, "out_codes", _U8),
                                 _ptr(out_scales, "out_scales", _U8), _stream(stream)), "kq_mx_quantize")
+    return out_codes, out_scales
+
+
+def kq_stream_probe(X, out_codes, out_scales, stream=None):
+    """Measurement only: the default quantizer's memory traffic with no arithmetic (outputs are a digest)."""
+    T, d = _shape(X)
+    _check(lib().kq_stream_probe(_ptr(X, "X", _BF16), T, d, _ptr(out_codes, "out_codes", _U8),
+                                 _ptr(out_scales, "out_scales", _U8), _stream(stream)), "kq_stream_probe")
     return out_codes, out_scales
 
 

@@ -180,8 +180,9 @@ kq_status run(int front, const uint16_t* X, int64_t tokens, int64_t d, const flo
   if (P && !aligned(P, 4)) return KQ_ERR_ALIGN;
   if (Kbf && !aligned(Kbf, 16)) return KQ_ERR_ALIGN;
   if (m && !aligned(m, 16)) return KQ_ERR_ALIGN;
-  if (mod && ((mod->stats && !aligned(mod->stats, 8)) || (mod->mscale && !aligned(mod->mscale, 4)) ||
-              (mod->mshift && !aligned(mod->mshift, 4))))
+  // the modulation vectors are read as 16-byte vectors (8 channels of a lane)
+  if (mod && ((mod->stats && !aligned(mod->stats, 8)) || (mod->mscale && !aligned(mod->mscale, 16)) ||
+              (mod->mshift && !aligned(mod->mshift, 16))))
     return KQ_ERR_ALIGN;
 
   const int64_t nb = d / 32;
@@ -445,6 +446,26 @@ kq_status kq_quantize_adaln(const uint16_t* X, int64_t tokens, int64_t d, const 
   const Mod mod{row_stats, mod_scale, mod_shift, tokens_per_sample};
   return run(kq::FRONT_KRON, X, tokens, d, K_params, params_block_stride, K_bf16, (int)variant, nullptr,
              nullptr, out_codes, out_scales, stream, &mod);
+}
+
+kq_status kq_stream_probe(const uint16_t* X, int64_t tokens, int64_t d, uint8_t* out_codes, uint8_t* out_scales,
+                          hipStream_t stream) {
+  kq_status st = check_shape(tokens, d);
+  if (st != KQ_OK) return st;
+  if (tokens == 0) return KQ_OK;
+  if (!X || !out_codes || !out_scales) return KQ_ERR_NULL;
+  if (!aligned(X, 16) || !aligned(out_codes, 16)) return KQ_ERR_ALIGN;
+  const uint64_t n = (uint64_t)tokens * (uint64_t)d;
+  const Range outs[] = {{out_codes, n / 2}, {out_scales, n / 32}};
+  const Range ins[] = {{X, n * 2}};
+  if (any_alias(outs, 2, ins, 1)) return KQ_ERR_ALIAS;
+  kq::FlatArgs a{};
+  a.X = X;
+  a.T = (int)tokens;
+  a.nb = (int)(d / 32);
+  a.codes = out_codes;
+  a.scales = out_scales;
+  return from_hip(kq::launch_flat(kq::FRONT_PROBE, false, a, stream));
 }
 
 kq_status kq_gemm_mx(const uint8_t* A_codes, const uint8_t* A_scales, int64_t M, const uint8_t* B_codes,

@@ -29,7 +29,9 @@
 // multiply by the product of the five diagonals.  All in fp32; the error
 // against the exact sum stays well below 1e-5 of the block amax.
 // FRONT_PLAIN: y = x.  FRONT_SMOOTH: y = x * m[c].  FRONT_HADAMARD: the
-// 32-point Walsh-Hadamard butterflies, then / sqrt(32).
+// 32-point Walsh-Hadamard butterflies, then / sqrt(32).  FRONT_PROBE: the
+// same loads, LDS round trip and stores with no arithmetic (a bandwidth
+// ceiling for this access pattern; its outputs are a digest, not codes).
 #include "kq_device.hpp"
 #include "kq_internal.h"
 
@@ -228,77 +230,83 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
 #pragma unroll
     for (int qq = 0; qq < 4; ++qq) w[qq] = *reinterpret_cast<const u32x4*>(stage + 16 * chunk_pos(lane, qq));
     float y[32];
-#pragma unroll
-    for (int qq = 0; qq < 4; ++qq)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        y[8 * qq + 2 * e] = bf16_lo(w[qq][e]);
-        y[8 * qq + 2 * e + 1] = bf16_hi(w[qq][e]);
-      }
-
-    if constexpr (FRONT == FRONT_KRON) {
-#pragma unroll
-      for (int k = 4; k >= 0; --k) {  // G5 (bit 0) first; the stages of different bits commute
-        const int bit = 1 << (4 - k);
-#pragma unroll
-        for (int c = 0; c < 32; ++c)
-          if (!(c & bit)) y[c] = fmaf(sl[k], y[c | bit], y[c]);
-#pragma unroll
-        for (int c = 0; c < 32; ++c)
-          if (!(c & bit)) y[c | bit] = fmaf(ss[k], y[c], y[c | bit]);
-      }
-#pragma unroll
-      for (int c = 0; c < 32; ++c) y[c] *= dg[c];
-    } else if constexpr (FRONT == FRONT_SMOOTH) {
-#pragma unroll
-      for (int c = 0; c < 32; ++c) y[c] *= mult[c];
-    } else if constexpr (FRONT == FRONT_HADAMARD) {
-#pragma unroll
-      for (int bit = 1; bit < 32; bit <<= 1)
-#pragma unroll
-        for (int c = 0; c < 32; ++c)
-          if (!(c & bit)) {
-            const float u = y[c], v = y[c | bit];
-            y[c] = u + v;
-            y[c | bit] = u - v;
-          }
-#pragma unroll
-      for (int c = 0; c < 32; ++c) y[c] *= 0.17677669529663688110021109052621225982120698f;  // 1/sqrt(32)
-    }
-
-    const float amax = absmax32(y);
-    unsigned byte = e8m0_byte(amax);
+    unsigned byte;
     u32x4 cw;
+    if constexpr (FRONT == FRONT_PROBE) {
+      cw = w[0] ^ w[1] ^ w[2] ^ w[3];
+      byte = cw[0] & 0xFFu;
+    } else {
 #pragma unroll
-    for (int qq = 0; qq < 4; ++qq) cw[qq] = pack_fp4(&y[8 * qq], byte);
-    if constexpr (kSum) {
-      if (amax == 0.0f) cw = u32x4{0u, 0u, 0u, 0u};  // an all-zero block of a sum gives +0 codes
-      // Blocks whose amax is within 2^-16 of a power of two are quantized
-      // again from exact values, one at a time by the whole wave, after the
-      // packing above (so that y need not stay in registers along this path).
-      const bool near = near_pow2(amax);
-      const uint64_t nearm = __builtin_amdgcn_ballot_w64(near);
-      if (__builtin_expect(nearm != 0, 0)) {
-        for (uint64_t m = nearm; m; m &= m - 1) {
-          const int L = __builtin_ctzll(m);
-          exact_block<FRONT>(stage, L, lds_p[FRONT == FRONT_KRON ? wv : 0][L], lds_ia[FRONT == FRONT_KRON ? wv : 0][L],
-                             lane, lds_res[wv][L],
-                             STORE_Y ? lds_ys[STORE_Y ? wv : 0] : nullptr);
-          __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          if constexpr (STORE_Y) {
-            if (lane == L) {
+      for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
-              for (int c = 0; c < 32; ++c) y[c] = lds_ys[wv][c];
+        for (int e = 0; e < 4; ++e) {
+          y[8 * qq + 2 * e] = bf16_lo(w[qq][e]);
+          y[8 * qq + 2 * e + 1] = bf16_hi(w[qq][e]);
+        }
+
+      if constexpr (FRONT == FRONT_KRON) {
+#pragma unroll
+        for (int k = 4; k >= 0; --k) {  // G5 (bit 0) first; the stages of different bits commute
+          const int bit = 1 << (4 - k);
+#pragma unroll
+          for (int c = 0; c < 32; ++c)
+            if (!(c & bit)) y[c] = fmaf(sl[k], y[c | bit], y[c]);
+#pragma unroll
+          for (int c = 0; c < 32; ++c)
+            if (!(c & bit)) y[c | bit] = fmaf(ss[k], y[c], y[c | bit]);
+        }
+#pragma unroll
+        for (int c = 0; c < 32; ++c) y[c] *= dg[c];
+      } else if constexpr (FRONT == FRONT_SMOOTH) {
+#pragma unroll
+        for (int c = 0; c < 32; ++c) y[c] *= mult[c];
+      } else if constexpr (FRONT == FRONT_HADAMARD) {
+#pragma unroll
+        for (int bit = 1; bit < 32; bit <<= 1)
+#pragma unroll
+          for (int c = 0; c < 32; ++c)
+            if (!(c & bit)) {
+              const float u = y[c], v = y[c | bit];
+              y[c] = u + v;
+              y[c | bit] = u - v;
             }
+#pragma unroll
+        for (int c = 0; c < 32; ++c) y[c] *= 0.17677669529663688110021109052621225982120698f;  // 1/sqrt(32)
+      }
+
+      const float amax = absmax32(y);
+      byte = e8m0_byte(amax);
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) cw[qq] = pack_fp4(&y[8 * qq], byte);
+      if constexpr (kSum) {
+        if (amax == 0.0f) cw = u32x4{0u, 0u, 0u, 0u};  // an all-zero block of a sum gives +0 codes
+        // Blocks whose amax is within 2^-16 of a power of two are quantized
+        // again from exact values, one at a time by the whole wave, after the
+        // packing above (so that y need not stay in registers along this path).
+        const bool near = near_pow2(amax);
+        const uint64_t nearm = __builtin_amdgcn_ballot_w64(near);
+        if (__builtin_expect(nearm != 0, 0)) {
+          for (uint64_t m = nearm; m; m &= m - 1) {
+            const int L = __builtin_ctzll(m);
+            exact_block<FRONT>(stage, L, lds_p[FRONT == FRONT_KRON ? wv : 0][L], lds_ia[FRONT == FRONT_KRON ? wv : 0][L],
+                               lane, lds_res[wv][L],
+                               STORE_Y ? lds_ys[STORE_Y ? wv : 0] : nullptr);
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             __builtin_amdgcn_wave_barrier();
+            if constexpr (STORE_Y) {
+              if (lane == L) {
+#pragma unroll
+                for (int c = 0; c < 32; ++c) y[c] = lds_ys[wv][c];
+              }
+              __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+              __builtin_amdgcn_wave_barrier();
+            }
           }
-        }
-        if (near) {
-          const unsigned* r = lds_res[wv][lane];
-          cw = u32x4{r[0], r[1], r[2], r[3]};
-          byte = r[4];
+          if (near) {
+            const unsigned* r = lds_res[wv][lane];
+            cw = u32x4{r[0], r[1], r[2], r[3]};
+            byte = r[4];
+          }
         }
       }
     }
@@ -351,6 +359,7 @@ hipError_t launch_flat(int front, bool store_y, const FlatArgs& args, hipStream_
     case FRONT_PLAIN: fn = pick<FRONT_PLAIN>(store_y); break;
     case FRONT_SMOOTH: fn = pick<FRONT_SMOOTH>(store_y); break;
     case FRONT_HADAMARD: fn = pick<FRONT_HADAMARD>(store_y); break;
+    case FRONT_PROBE: fn = (const void*)&flat_kernel<FRONT_PROBE, false>; break;
     default: return hipErrorInvalidValue;
   }
   FlatArgs a = args;
