@@ -70,6 +70,25 @@
  * returns KQ_ERR_HIP.  Faults inside a kernel surface at the caller's next
  * synchronization, as for any asynchronous HIP work.  No C++ exception
  * crosses this boundary.
+ *
+ * Interface notes (where these calls go beyond the plain form
+ * kq_quantize(X, d, K_params, codes, scales, stream)):
+ *   - every quantizing entry point takes `tokens`, the row count of X;
+ *   - kq_quantize_ex takes no term count for K_bf16: KQ_MFMA_DENSE always
+ *     reads the three-term split.  One bf16 term keeps 8 significant bits of
+ *     each entry of K and two keep 16, so the transform error is bounded
+ *     only by about 2^-9 or 2^-17 of sum_r |x_r K_rc|, which is above 1e-5
+ *     of the block amax as soon as that sum exceeds 1.3 times the amax (as
+ *     it does for most blocks); only three terms (the fp32 K exactly) keep
+ *     the error within 1e-5 for every K.  kq_build_blocks still writes 1 to
+ *     3 terms for other consumers;
+ *   - kq_transform_f32 is one diagnostic entry for every front-end: it takes
+ *     the front-end, the parameter stride, K_bf16 and ch_mult, and writes the
+ *     codes and scales beside Y, so that each quantizing entry point's own
+ *     kernel (plus a Y store) is what a test checks, codes included;
+ *   - KQ_ERR_ALIAS: overlapping ranges are rejected with their own status
+ *     rather than left undefined, since with an overlap the result would
+ *     depend on the order in which the workgroups run.
  */
 #ifndef KQ_H
 #define KQ_H
@@ -326,7 +345,9 @@ kq_status kq_gemm_mx(const uint8_t* A_codes, const uint8_t* A_scales, int64_t M,
  * kq_quantize's default kernel on X [tokens][d] (every bf16 of X read once in
  * 4 KB units of 64 consecutive 32-channel blocks, one 16-byte record per
  * block written to out_codes [tokens][d/2] and one byte per block to
- * out_scales [tokens][d/32], the same grid and unit order) with no arithmetic:
+ * out_scales [tokens][d/32], each wave's units in the same order, through the
+ * same wave-private LDS round trip; the grid is sized for the probe's own
+ * occupancy, one resident round of waves) with no arithmetic:
  * the outputs hold an XOR digest of the input, not codes.  Its rate is the
  * ceiling this access pattern reaches on the device, against which the
  * quantizers' rates are reported (the Pith review's Fig. 3 reports the

@@ -30,9 +30,6 @@
 #include "kq_device.hpp"
 #include "kq_internal.h"
 
-#ifndef GROUPM
-#define GROUPM 4
-#endif
 namespace kq {
 
 namespace {
@@ -45,7 +42,7 @@ constexpr int kBM = 256, kBN = 256;  // tile of Y
 constexpr int kStages = 4;           // LDS ring
 constexpr int kRowB = 64;            // bytes per staged row (128 K values)
 constexpr int kTileB = kBM * kRowB;  // 16 KB per operand per stage
-constexpr int kGroupM = GROUPM;      // M tiles per group of the tile order
+constexpr int kGroupM = 4;           // M tiles per group of the tile order
 constexpr int kScB = kBM * 16;       // scale bytes per operand per group of 4 stages: [row][16 K blocks]
 
 // Loads into LDS issued as asm, so that the compiler inserts no waits of its
