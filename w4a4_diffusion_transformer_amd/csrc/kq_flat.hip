@@ -88,16 +88,17 @@ __device__ __forceinline__ float max32(float v) {
 // of the exact products x[r] K32[r][c] (KRON) or of (-1)^popcount(r & c) x[r]
 // then divided by sqrt(32) (HADAMARD), rounded once to fp32.  K32[r][c] is
 // the fp64 product, in factor order, of one entry per factor (G1 on bit 4),
-// rounded to fp32, with G = [[a, b], [l a, l b + 1/a]] in fp64: the block's
-// 15 scalars p15 and the five fp64 quotients 1/a come from LDS.  The block is
-// then quantized from these values: res receives its four code words and its
-// scale byte, ys (if not null) the 32 values.  Everything after the first
+// rounded to fp32, with G = [[a, b], [l a, l b + 1/a]] in fp64 from the
+// block's 15 scalars p15 (kept in LDS by the kernel's setup; the quotients
+// 1/a are formed here, so that the common path carries no fp64 division).
+// The block is then quantized from these values: res receives its four code
+// words and its scale byte, ys (if not null) the 32 values.  Everything after the first
 // reads runs in registers, so that a wave meeting such a block is held up
 // only briefly.  Not inlined: the kernel's register allocation stays that of
 // its common path.
 template <int FRONT>
-__device__ __attribute__((noinline)) void exact_block(const uint8_t* stage, int b, const float* p15,
-                                                      const double* inv_a, int lane, unsigned* res, float* ys) {
+__device__ __attribute__((noinline)) void exact_block(const uint8_t* stage, int b, const float* p15, int lane,
+                                                      unsigned* res, float* ys) {
   const int c = lane & 31;
   u32x4 w[4];
 #pragma unroll
@@ -114,7 +115,7 @@ __device__ __attribute__((noinline)) void exact_block(const uint8_t* stage, int 
       const double L = p15[3 * k], A = p15[3 * k + 1], B = p15[3 * k + 2];
       const bool bit = (c >> (4 - k)) & 1;
       e0[k] = bit ? B : A;
-      e1[k] = bit ? fma(L, B, inv_a[k]) : L * A;  // l b is exact in fp64: one rounding, as l b + 1/a
+      e1[k] = bit ? fma(L, B, 1.0 / A) : L * A;  // l b is exact in fp64: one rounding, as l b + 1/a
     }
 #pragma unroll
     for (int r = 0; r < 32; ++r) {
@@ -142,24 +143,29 @@ __device__ __attribute__((noinline)) void exact_block(const uint8_t* stage, int 
 template <int FRONT, bool STORE_Y>
 __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
   __shared__ __attribute__((aligned(256))) uint8_t lds_x[kWaves][kUnitBytes];
-  // exact path: each lane's 15 scalars and its five fp64 quotients 1/a
-  __shared__ float lds_p[FRONT == FRONT_KRON ? kWaves : 1][64][15];
-  __shared__ double lds_ia[FRONT == FRONT_KRON ? kWaves : 1][64][5];
+  __shared__ float lds_p[FRONT == FRONT_KRON ? kWaves : 1][64][15];  // exact path: each lane's 15 scalars
   constexpr bool kSum = FRONT == FRONT_KRON || FRONT == FRONT_HADAMARD;  // fronts with an exact path
   __shared__ unsigned lds_res[kSum ? kWaves : 1][64][5];   // exact path: code words and byte per lane
   __shared__ float lds_ys[kSum && STORE_Y ? kWaves : 1][32];  // exact path: the values (diagnostic Y)
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int gw = __builtin_amdgcn_readfirstlane((int)blockIdx.x * kWaves + wv);
-  const int nph = a.phases;
-  if (gw >= nph * a.chunks) return;  // wave-uniform; nothing below synchronizes the workgroup
-  const int ph = gw % nph, chk = gw / nph;
-  const int64_t u0 = ph + (int64_t)nph * chk;         // first unit
-  const int64_t ustep = (int64_t)nph * a.chunks;      // units between this wave's units
-  const int n = u0 < a.units ? (int)((a.units - 1 - u0) / ustep) + 1 : 0;
-  if (n == 0) return;
-  const int j = (int)((64 * (int64_t)ph + lane) % a.nb);  // this lane's block column, for every unit
+  // consecutive waves take consecutive phases (the four waves of a
+  // workgroup stream adjacent units); unit indices stay below 2^29
+  // (tokens * d < 2^40), so the index arithmetic is 32-bit
+  const unsigned gw = (unsigned)__builtin_amdgcn_readfirstlane((int)blockIdx.x * kWaves + wv);
+  const unsigned nph = (unsigned)a.phases;
+  if (gw >= nph * (unsigned)a.chunks) return;  // wave-uniform; nothing below synchronizes the workgroup
+  const int ph = (int)(gw % nph), chk = (int)(gw / nph);
+  const unsigned u0 = (unsigned)ph + (unsigned)a.phases * (unsigned)chk;  // first unit
+  const unsigned ustep = (unsigned)a.phases * (unsigned)a.chunks;        // units between this wave's units
+  const unsigned units = (unsigned)a.units;
+  if (u0 >= units) return;
+  const int n = (int)((units - 1 - u0) / ustep) + 1;
+  // this lane's block column, for every unit: (64 ph + lane) mod nb
+  const unsigned nb = (unsigned)a.nb;
+  const unsigned j0 = (64u * (unsigned)ph) % nb;  // wave-uniform
+  const int j = (int)(nb >= 64 ? (j0 + lane >= nb ? j0 + lane - nb : j0 + lane) : (j0 + lane) % nb);
   uint8_t* stage = lds_x[wv];
 
   // ---- per-lane coefficients of block column j
@@ -175,7 +181,6 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
       lds_p[wv][lane][3 * k] = sl[k];  // for the exact path
       lds_p[wv][lane][3 * k + 1] = av;
       lds_p[wv][lane][3 * k + 2] = bv;
-      lds_ia[wv][lane][k] = 1.0 / (double)av;
       ss[k] = av * bv;
       da[k] = av;
       ia[k] = 1.0f / av;
@@ -202,9 +207,9 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
   }
 
   // ---- wave-uniform cursors: the next unit to load, the unit being stored
-  const int64_t lstep = ustep * kUnitBytes;
-  const uint8_t* lx = reinterpret_cast<const uint8_t*>(a.X) + u0 * kUnitBytes;
-  int64_t lleft = a.xbytes - u0 * kUnitBytes;  // bytes from the load cursor to the end of X
+  const int64_t lstep = (int64_t)ustep * kUnitBytes;
+  const uint8_t* lx = reinterpret_cast<const uint8_t*>(a.X) + (int64_t)u0 * kUnitBytes;
+  int64_t lleft = a.xbytes - (int64_t)u0 * kUnitBytes;  // bytes from the load cursor to the end of X
   auto clamp_bytes = [](int64_t left, int unit) { return left <= 0 ? 0 : (left >= unit ? unit : (int)left); };
   u32x4 pre[kDepth][4];
   auto load = [&](int slot) {
@@ -215,8 +220,8 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
     lx += lstep;
     lleft -= lstep;
   };
-  int64_t ub = u0 * kUnitBlocks;  // first block of the unit being computed
-  const int64_t bstep = ustep * kUnitBlocks;
+  int64_t ub = (int64_t)u0 * kUnitBlocks;  // first block of the unit being computed
+  const int64_t bstep = (int64_t)ustep * kUnitBlocks;
 
   auto compute = [&](int slot) {
     // stage: 1 KB load i holds 16-byte chunk 64 i + lane = quarter (lane & 3) of block 16 i + lane / 4
@@ -288,8 +293,7 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
         if (__builtin_expect(nearm != 0, 0)) {
           for (uint64_t m = nearm; m; m &= m - 1) {
             const int L = __builtin_ctzll(m);
-            exact_block<FRONT>(stage, L, lds_p[FRONT == FRONT_KRON ? wv : 0][L], lds_ia[FRONT == FRONT_KRON ? wv : 0][L],
-                               lane, lds_res[wv][L],
+            exact_block<FRONT>(stage, L, lds_p[FRONT == FRONT_KRON ? wv : 0][L], lane, lds_res[wv][L],
                                STORE_Y ? lds_ys[STORE_Y ? wv : 0] : nullptr);
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             __builtin_amdgcn_wave_barrier();
