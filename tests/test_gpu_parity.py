@@ -362,6 +362,26 @@ def test_error_codes_on_device_buffers():
     assert L.kq_quantize(X.data_ptr(), 4, 48, P.data_ptr(), codes.data_ptr(), scales.data_ptr(), None) == 2
 
 
+@pytest.mark.parametrize("T,d", [(7, 96), (33, 2240), (129, 3072), (5, 32), (300, 1152)])
+def test_stream_probe_digest(T, d):
+    """kq_stream_probe moves the default kernel's traffic with no arithmetic: its record for each
+    32-channel block is the XOR of the block's four 16-byte quarters and its scale byte the record's
+    first byte.  Checked against that host evaluation on every block, ragged last units included, so
+    the probe (and the unit, phase and lane addressing it shares with the quantizer) touches every
+    block exactly once and in place."""
+    rng = np.random.default_rng(T * 7 + d)
+    X = rng.integers(0, 1 << 16, size=(T, d), dtype=np.uint16)
+    Xd = dev(X)
+    codes = torch.full((T, d // 2), 0xA5, dtype=torch.uint8, device="cuda:0")
+    scales = torch.full((T, d // 32), 0x5A, dtype=torch.uint8, device="cuda:0")
+    kq.kq_stream_probe(Xd, codes, scales)
+    torch.cuda.synchronize()
+    blocks = X.view(np.uint8).reshape(T * (d // 32), 4, 16)
+    rec = blocks[:, 0] ^ blocks[:, 1] ^ blocks[:, 2] ^ blocks[:, 3]
+    np.testing.assert_array_equal(host(codes).reshape(-1, 16), rec)
+    np.testing.assert_array_equal(host(scales).reshape(-1), rec[:, 0])
+
+
 # ---------------------------------------------------------------- full-size workloads
 
 
