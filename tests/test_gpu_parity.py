@@ -165,6 +165,36 @@ def test_edge_shapes(variant, shape):
     check_kron(X, P, variant)
 
 
+# The boundary's extremes: the largest d it accepts (2^24 channels = 2^19 blocks per row, a power of
+# two), one block less (2^19 - 1 blocks: as many unit phases in the default kernel's grid, over 131k
+# workgroups), and the smallest d (one block per row) with 2^20 rows.
+EXTREME_SHAPES = [(2, 1 << 24), (3, (1 << 24) - 32), (1 << 20, 32)]
+
+
+_EXTREME = {}
+
+
+def extreme_case(shape):
+    """Inputs and the oracle's result for one extreme shape, computed once (the oracle builds K for
+    2^19 blocks here, some seconds per row)."""
+    if shape not in _EXTREME:
+        T, d = shape
+        X = synth.random_matrix(T, d, seed=T + d % 1000, n_outliers=max(1, d // 1000), mult=60.0)
+        P = synth.random_params(d // 32, seed=(d + 11) % 100003)
+        _EXTREME[shape] = (X, P, oracle_ref(oracle.KRON, X, P))
+    return _EXTREME[shape]
+
+
+@pytest.mark.parametrize("shape", EXTREME_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+@pytest.mark.parametrize("variant", ["butterfly", "mfma_otf"])
+def test_extreme_shapes(variant, shape):
+    X, P, ref = extreme_case(shape)
+    codes, scales, _ = run_kron(X, P, variant)
+    rep = compare(codes, scales, ref["codes"], ref["scales"], yhat_fn(oracle.KRON, X, P))
+    record(f"extreme {shape[0]}x{shape[1]} {variant}", rep)
+    assert rep.ok(), f"{variant}: {rep}"
+
+
 @pytest.mark.parametrize("variant", list(VARIANTS))
 def test_shared_k_stride_zero(variant):
     X = synth.random_matrix(200, 2240, seed=5, n_outliers=45, mult=80.0)
