@@ -233,8 +233,16 @@ kq_status run(int front, const uint16_t* X, int64_t tokens, int64_t d, const flo
     return from_hip(
         kq::launch_mfma(variant == KQ_MFMA_OTF ? KSRC_PARAMS : KSRC_SPLIT, Y != nullptr, mod != nullptr, a, stream));
   }
-  if (front == kq::FRONT_KRON) {  // KQ_BUTTERFLY
+  // One block per lane (kq_flat.hip): KroQuant's butterfly, and the comparison front-ends where it
+  // is the faster layout (measured on MI355X at the PixArt, SANA, FLUX and stress matrices): plain
+  // and Hadamard-32 at every shape, SmoothQuant from 2^24 elements on (below that, its 32
+  // multipliers per lane make the per-wave setup cost more than the row layout of kq_quad.hip).
+  const bool flat = front == kq::FRONT_KRON || front == kq::FRONT_PLAIN ||
+                    (front == kq::FRONT_HADAMARD && hblock == 32) ||
+                    (front == kq::FRONT_SMOOTH && T * d >= (int64_t(1) << 24));
+  if (flat) {
     kq::FlatArgs a{};
+    a.m = m;
     a.X = X;
     a.T = T;
     a.nb = (int)nb;
