@@ -217,7 +217,8 @@ def adaln_table(kq, torch, np, synth, dev):
     Unfused: a LayerNorm + modulation written as torch ops (fp32 math, one bf16
     tensor written back to HBM) followed by kq_quantize on that tensor.  Fused:
     kq_quantize_adaln on the raw activation with the row statistics.  The row
-    statistics kernel is timed on its own.  Inputs: FLUX.1-schnell width
+    statistics kernel is timed on its own, and the fused step also on the MFMA kernel (mfma_otf).
+    Inputs: FLUX.1-schnell width
     (one sample of 4608 tokens x 3072) and PixArt-Sigma width (2 x 4096 tokens
     x 1152), N(0,1) activations with 1% outlier channels, AdaLN vectors with 1%
     amplified channels."""
@@ -250,6 +251,10 @@ def adaln_table(kq, torch, np, synth, dev):
             return L.kq_quantize_adaln(xs[i], T, d, stp[i], scd.data_ptr(), shd.data_ptr(), tps, Pd.data_ptr(), 15,
                                        None, kq.KQ_AUTO, *ops[i], stream)
 
+        def fused_otf(i):
+            return L.kq_quantize_adaln(xs[i], T, d, stp[i], scd.data_ptr(), shd.data_ptr(), tps, Pd.data_ptr(), 15,
+                                       None, kq.KQ_MFMA_OTF, *ops[i], stream)
+
         def stats(i):
             return L.kq_row_stats(xs[i], T, d, 1e-6, stp[i], stream)
 
@@ -259,11 +264,12 @@ def adaln_table(kq, torch, np, synth, dev):
             return L.kq_quantize_ex(xm.data_ptr(), T, d, Pd.data_ptr(), 15, None, kq.KQ_AUTO, *ops[i], stream)
 
         row = {"T": T, "d": d, "tokens_per_sample": tps}
-        for label, fn in (("fused_quantize_adaln", fused), ("row_stats", stats), ("unfused_torch_eager_modulate_then_quantize", unfused)):
+        for label, fn in (("fused_quantize_adaln", fused), ("fused_quantize_adaln_mfma_otf", fused_otf), ("row_stats", stats),
+                          ("unfused_torch_eager_modulate_then_quantize", unfused)):
             secs = time_calls(torch, fn, [(i,) for i in range(copies)], max(60, 4 * copies))
             sec = secs[len(secs) // 2]
             row[label] = {"us": round(sec * 1e6, 2), "us_min": round(secs[0] * 1e6, 2), "us_max": round(secs[-1] * 1e6, 2)}
-            if label == "fused_quantize_adaln":
+            if label.startswith("fused_quantize_adaln"):
                 fb = nbytes + 8 * T
                 row[label].update({"GBps": round(fb / sec / 1e9, 1), "pct_peak": round(100 * fb / sec / 1e9 / HBM_PEAK_GBS, 1)})
             if label == "row_stats":

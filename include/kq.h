@@ -299,10 +299,10 @@ kq_status kq_row_stats(const uint16_t* X, int64_t tokens, int64_t d, float eps, 
  * where diffusion differs from an LLM" describes AdaLN as timestep-dependent
  * per-channel scales and shifts; the form v (1 + scale) + shift is the DiT
  * one).  tokens_per_sample must be a multiple of 32 or at least tokens
- * (KQ_ERR_SHAPE otherwise).  Variants: KQ_AUTO, KQ_MFMA_OTF, KQ_MFMA_DENSE
- * with the same inputs as kq_quantize_ex; KQ_BUTTERFLY -> KQ_ERR_VARIANT
- * (KQ_AUTO never resolves to it here: where KQ_VARIANT or a kq_tune record
- * names the butterfly, this entry point takes KQ_MFMA_OTF).
+ * (KQ_ERR_SHAPE otherwise).  Variants as kq_quantize_ex, with the same
+ * inputs and the same rule for KQ_AUTO: every variant applies the producer
+ * step, and the codes and scales equal those kq_quantize_ex gives with that
+ * variant on the modulated bf16 matrix, bit for bit.
  * row_stats must be 8-byte aligned, mod_scale / mod_shift 16-byte aligned
  * (KQ_ERR_ALIGN otherwise).
  */

@@ -173,7 +173,7 @@ def test_quantize_adaln_argument_checks(lib):
     assert q(A, 100, 64, B, C, D, 0, E, 15, None, 0, F, G, None) == KQ_ERR_SHAPE
     assert q(A, 100, 64, B, C, D, 40, E, 15, None, 0, F, G, None) == KQ_ERR_SHAPE
     assert q(A, 100, 64, B, C, D, 64, E, 7, None, 0, F, G, None) == KQ_ERR_SHAPE
-    assert q(A, 100, 64, B, C, D, 64, E, 15, None, 3, F, G, None) == KQ_ERR_VARIANT
+    assert q(A, 100, 64, B, C, D, 64, E, 15, None, -1, F, G, None) == KQ_ERR_VARIANT
     assert q(A, 100, 64, B, C, D, 64, E, 15, None, 9, F, G, None) == KQ_ERR_VARIANT
     assert q(A, 0, 64, None, None, None, 64, None, 15, None, 0, None, None, None) == KQ_OK
     assert q(A, 100, 64, B, C, D, 64, None, 15, None, 0, F, G, None) == KQ_ERR_VARIANT

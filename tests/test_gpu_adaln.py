@@ -83,10 +83,15 @@ def run_fused(X, P, st, sc, sh, tps, variant):
     return host(codes), host(scales)
 
 
-def run_plain_kron(Xmod, P):
+def run_plain_kron(Xmod, P, variant=kq.KQ_MFMA_OTF):
     Xd = dev(Xmod)
     codes, scales = kq.alloc_outputs(Xd)
-    kq.kq_quantize_ex(Xd, dev(P), 15, None, kq.KQ_MFMA_OTF, codes, scales)
+    Pd, Kbf = dev(P), None
+    if variant == kq.KQ_MFMA_DENSE:
+        Kbf = torch.empty((P.shape[0], 3, 32, 32), dtype=torch.int16, device="cuda:0")
+        kq.kq_build_blocks(Pd, P.shape[0], None, Kbf, 3)
+        Pd = None
+    kq.kq_quantize_ex(Xd, Pd, 15, Kbf, variant, codes, scales)
     torch.cuda.synchronize()
     return host(codes), host(scales)
 
@@ -103,8 +108,9 @@ def check(name, X, P, st, sc, sh, tps, variant, against_unfused=True):
     rep = compare(codes, scales, ref["codes"], ref["scales"], yh)
     record(name, rep)
     assert rep.ok(), f"{name}: {rep}"
-    if against_unfused and variant == kq.KQ_MFMA_OTF:
-        c2, s2 = run_plain_kron(Xmod, P)
+    if against_unfused:
+        # the same variant on the oracle's modulated matrix: bit for bit
+        c2, s2 = run_plain_kron(Xmod, P, variant)
         np.testing.assert_array_equal(scales, s2)
         np.testing.assert_array_equal(codes, c2)
 
@@ -148,7 +154,7 @@ MODES = {
 
 @pytest.mark.parametrize("mode", list(MODES))
 @pytest.mark.parametrize("T,d,tps", [(64, 1152, 32), (300, 3072, 300), (257, 2240, 128), (96, 5600, 64)])
-@pytest.mark.parametrize("variant", [2, 1])
+@pytest.mark.parametrize("variant", [3, 2, 1])
 def test_fused_small(T, d, tps, mode, variant):
     X, P, st, sc, sh = inputs(T, d, tps, seed=T * 7 + d)
     us, usc, ush = MODES[mode]
@@ -156,10 +162,11 @@ def test_fused_small(T, d, tps, mode, variant):
           sh if ush else None, tps, variant)
 
 
-def test_fused_without_producer_inputs_equals_quantizer():
+@pytest.mark.parametrize("variant", [3, 2])
+def test_fused_without_producer_inputs_equals_quantizer(variant):
     X, P, _, _, _ = inputs(200, 1152, 200, seed=5)
-    codes, scales = run_fused(X, P, None, None, None, 200, kq.KQ_MFMA_OTF)
-    c2, s2 = run_plain_kron(X, P)
+    codes, scales = run_fused(X, P, None, None, None, 200, variant)
+    c2, s2 = run_plain_kron(X, P, variant)
     np.testing.assert_array_equal(codes, c2)
     np.testing.assert_array_equal(scales, s2)
 
@@ -169,9 +176,10 @@ def test_fused_without_producer_inputs_equals_quantizer():
     ("pixart_x1", 8192, 1152, 4096, synth.BASE_NORMAL),      # PixArt-Sigma width, batch 2 x 4096 tokens
     ("sana_x1", 4096, 2240, 1024, synth.BASE_NORMAL),        # SANA width, batch 4 x 1024 tokens
 ])
-def test_fused_full_workloads(name, T, d, tps, kind):
+@pytest.mark.parametrize("variant", [0, 2], ids=["auto", "mfma_otf"])
+def test_fused_full_workloads(name, T, d, tps, kind, variant):
     X, P, st, sc, sh = inputs(T, d, tps, seed={"flux_x1": 31, "pixart_x1": 32, "sana_x1": 33}[name], kind=kind)
-    check(f"adaln {name}", X, P, st, sc, sh, tps, kq.KQ_MFMA_OTF)
+    check(f"adaln {name} v{variant}", X, P, st, sc, sh, tps, variant)
 
 
 def test_modulation_vectors_at_an_offset():
@@ -207,8 +215,8 @@ def test_fused_error_codes():
     with pytest.raises(kq.KQError) as e:
         kq.kq_quantize_adaln(Xd, dev(st), dev(sc), dev(sh), 40, dev(P), codes, scales)
     assert e.value.status == 2
-    with pytest.raises(kq.KQError) as e:
-        kq.kq_quantize_adaln(Xd, dev(st), dev(sc), dev(sh), 64, dev(P), codes, scales, 15, None, kq.KQ_BUTTERFLY)
+    with pytest.raises(kq.KQError) as e:  # the prebuilt-split variant without a split
+        kq.kq_quantize_adaln(Xd, dev(st), dev(sc), dev(sh), 64, dev(P), codes, scales, 15, None, kq.KQ_MFMA_DENSE)
     assert e.value.status == 4
 
 
@@ -224,25 +232,25 @@ P = torch.from_numpy(synth.random_params(d // 32, seed=4)).cuda()
 sc, sh = (torch.from_numpy(a).cuda() for a in synth.adaln_vectors(1, d, seed=5))
 st = torch.empty((T, 2), dtype=torch.float32, device="cuda")
 kq.kq_row_stats(X, 1e-6, st)
-assert kq.kq_auto_variant(T, d, True, False) == kq.KQ_BUTTERFLY, "override not in effect"
+assert kq.kq_auto_variant(T, d, True, False) == kq.KQ_MFMA_OTF, "override not in effect"
 auto = kq.kq_quantize_adaln(X, st, sc, sh, T, P, *kq.alloc_outputs(X))
 otf = kq.kq_quantize_adaln(X, st, sc, sh, T, P, *kq.alloc_outputs(X), variant=kq.KQ_MFMA_OTF)
 plain = kq.kq_quantize_ex(X, P, 15, None, kq.KQ_AUTO, *kq.alloc_outputs(X))
 torch.cuda.synchronize()
-assert all(torch.equal(a, b) for a, b in zip(auto, otf)), "AUTO under the butterfly override differs from mfma_otf"
+assert all(torch.equal(a, b) for a, b in zip(auto, otf)), "AUTO under the mfma_otf override differs from mfma_otf"
 assert not torch.equal(auto[0], plain[0]), "modulation not applied"
 print("ok")
 """
 
 
-def test_auto_under_butterfly_override_keeps_the_producer_step():
-    """With KQ_VARIANT=butterfly (read once per process, hence a child
-    process), KQ_AUTO resolves to the butterfly for the plain quantizer, and the
-    fused AdaLN entry point, which has no butterfly form, takes mfma_otf: same
-    bytes as an explicit mfma_otf call, and not the unmodulated quantization."""
+def test_auto_follows_the_variant_override():
+    """With KQ_VARIANT=mfma_otf (read once per process, hence a child
+    process), KQ_AUTO resolves to mfma_otf for the fused AdaLN entry point as
+    for the plain quantizer: the same bytes as an explicit mfma_otf call, and
+    not the unmodulated quantization."""
     import subprocess
     import sys
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-    env = dict(os.environ, KQ_VARIANT="butterfly")
+    env = dict(os.environ, KQ_VARIANT="mfma_otf")
     r = subprocess.run([sys.executable, "-c", _CHILD, root], env=env, capture_output=True, text=True, timeout=180)
     assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout[-2000:] + r.stderr[-2000:]

@@ -160,19 +160,13 @@ kq_status run(int front, const uint16_t* X, int64_t tokens, int64_t d, const flo
   if (mod) {
     // a tile of 32 rows never straddles two samples
     if (mod->tps <= 0 || (mod->tps % 32 != 0 && mod->tps < tokens)) return KQ_ERR_SHAPE;
-    if (variant == KQ_BUTTERFLY || front != kq::FRONT_KRON) return KQ_ERR_VARIANT;
+    if (front != kq::FRONT_KRON) return KQ_ERR_VARIANT;
   }
   if (tokens == 0) return KQ_OK;
   if (!X || !codes || !scales) return KQ_ERR_NULL;
   if (front == kq::FRONT_SMOOTH && !m) return KQ_ERR_NULL;
   if (front == kq::FRONT_KRON) {
-    if (variant == KQ_AUTO) {
-      variant = auto_variant(tokens, d, P != nullptr, Kbf != nullptr);
-      // the producer step is fused into the MFMA kernels only: a butterfly
-      // choice (KQ_VARIANT, or a kq_tune record for this shape) yields to the
-      // K-from-scalars MFMA kernel, which takes the same inputs
-      if (mod && variant == KQ_BUTTERFLY) variant = KQ_MFMA_OTF;
-    }
+    if (variant == KQ_AUTO) variant = auto_variant(tokens, d, P != nullptr, Kbf != nullptr);
     if (variant == KQ_MFMA_DENSE && !Kbf) return KQ_ERR_VARIANT;
     if (variant != KQ_MFMA_DENSE && !P) return KQ_ERR_VARIANT;
   }
@@ -243,6 +237,13 @@ kq_status run(int front, const uint16_t* X, int64_t tokens, int64_t d, const flo
   if (flat) {
     kq::FlatArgs a{};
     a.m = m;
+    if (mod) {  // the producer step in front of the butterfly
+      front = kq::FRONT_ADALN;
+      a.stats = mod->stats;
+      a.mscale = mod->mscale;
+      a.mshift = mod->mshift;
+      a.tps = mod->tps;
+    }
     a.X = X;
     a.T = T;
     a.nb = (int)nb;

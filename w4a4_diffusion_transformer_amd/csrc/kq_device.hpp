@@ -23,6 +23,8 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 enum { FRONT_KRON = 0, FRONT_PLAIN = 1, FRONT_SMOOTH = 2, FRONT_HADAMARD = 3 };
 // Measurement only: the quantizer's memory traffic with no arithmetic.
 enum { FRONT_PROBE = 4 };
+// KroQuant with the AdaLN producer step in front of the transform (block-per-lane kernel).
+enum { FRONT_ADALN = 5 };
 enum { LAYOUT_MFMA = 0, LAYOUT_QUAD = 1 };
 
 // Half-width of the window around a power of two inside which a block's

@@ -29,7 +29,8 @@
 // multiply by the product of the five diagonals.  All in fp32; the error
 // against the exact sum stays well below 1e-5 of the block amax.
 // FRONT_PLAIN: y = x.  FRONT_SMOOTH: y = x * m[c].  FRONT_HADAMARD: the
-// 32-point Walsh-Hadamard butterflies, then / sqrt(32).  FRONT_PROBE: the
+// 32-point Walsh-Hadamard butterflies, then / sqrt(32).  FRONT_ADALN: the
+// AdaLN producer step, then KRON (below, at modulate32).  FRONT_PROBE: the
 // same loads, LDS round trip and stores with no arithmetic (a bandwidth
 // ceiling for this access pattern; its outputs are a digest, not codes).
 #include "kq_device.hpp"
@@ -79,6 +80,39 @@ __device__ __forceinline__ float max32(float v) {
   const unsigned u = __float_as_uint(v);
   const auto sw = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // rows 0 <-> 1, 2 <-> 3
   return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+// The AdaLN producer step of one block (the handbook page "Quantization:
+// where diffusion differs from an LLM" gives AdaLN as timestep-dependent
+// per-channel scales and shifts; the form v (1 + scale) + shift is the
+// DiT one): per value, in fp32 and in this order with no contraction,
+// v = ((x - mean) * rstd) * opa + sh, rounded to bf16 (nearest even).  An
+// absent input is an identity operand (mean +0, rstd 1, opa 1, sh -0), which
+// leaves v exactly x, signed zeros included.  y[c] receives the bf16 value
+// as fp32; w (if not null) the bf16 pairs, even channel in the low half.
+__device__ __forceinline__ void modulate32(const u32x4 x[4], float mean, float rstd, const float opa[32],
+                                           const float sh[32], float y[32], u32x4* w) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      unsigned pair = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = 8 * qq + 2 * e + h;
+        float v = h ? bf16_hi(x[qq][e]) : bf16_lo(x[qq][e]);
+        v = v - mean;
+        v = v * rstd;
+        v = v * opa[c];
+        v = v + sh[c];
+        const __bf16 b = (__bf16)v;
+        const unsigned bits = __builtin_bit_cast(unsigned short, b);
+        y[c] = __uint_as_float(bits << 16);
+        pair |= bits << (16 * h);
+      }
+      if (w) w[qq][e] = pair;
+    }
 }
 
 // Exact quantization of block b of the staged unit, by the whole wave: a
@@ -143,8 +177,9 @@ __device__ __attribute__((noinline)) void exact_block(const uint8_t* stage, int 
 template <int FRONT, bool STORE_Y>
 __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
   __shared__ __attribute__((aligned(256))) uint8_t lds_x[kWaves][kUnitBytes];
-  __shared__ float lds_p[FRONT == FRONT_KRON ? kWaves : 1][64][15];  // exact path: each lane's 15 scalars
-  constexpr bool kSum = FRONT == FRONT_KRON || FRONT == FRONT_HADAMARD;  // fronts with an exact path
+  constexpr bool kKron = FRONT == FRONT_KRON || FRONT == FRONT_ADALN;  // fronts with KroQuant's transform
+  __shared__ float lds_p[kKron ? kWaves : 1][64][15];                  // exact path: each lane's 15 scalars
+  constexpr bool kSum = kKron || FRONT == FRONT_HADAMARD;              // fronts with an exact path
   __shared__ unsigned lds_res[kSum ? kWaves : 1][64][5];   // exact path: code words and byte per lane
   __shared__ float lds_ys[kSum && STORE_Y ? kWaves : 1][32];  // exact path: the values (diagnostic Y)
 
@@ -171,7 +206,7 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
   // ---- per-lane coefficients of block column j
   float sl[5], ss[5], dg[32];  // KRON: shear l, shear a b (G1 .. G5), product of the diagonals
   float mult[32];              // SMOOTH
-  if constexpr (FRONT == FRONT_KRON) {
+  if constexpr (kKron) {
     const float* p = a.P + (int64_t)j * a.pstride;
     float da[5], ia[5];
 #pragma unroll
@@ -206,6 +241,49 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
     }
   }
 
+  // ---- ADALN: the row of this lane's block in the unit being loaded and in
+  // the one being computed (each unit step advances it by rows_step), and
+  // the lane's (1 + scale, shift) for its 32 channels of sample cur_s
+  unsigned lrow = 0, crow = 0;
+  int cur_s = -1;
+  float opa[32], sh[32];
+  // ADALN: loads (1 + scale, shift) for this lane's 32 channels of sample smp
+  auto load_mod = [&](int smp) {
+    const int64_t off = (int64_t)smp * (32 * (int64_t)a.nb) + 32 * j;
+    if (a.mscale) {  // uniform
+      const f32x4* mp = reinterpret_cast<const f32x4*>(a.mscale + off);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const f32x4 v = mp[k];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) opa[4 * k + i] = 1.0f + v[i];
+      }
+    }
+    if (a.mshift) {  // uniform
+      const f32x4* hp = reinterpret_cast<const f32x4*>(a.mshift + off);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const f32x4 v = hp[k];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sh[4 * k + i] = v[i];
+      }
+    }
+    cur_s = smp;
+  };
+  if constexpr (FRONT == FRONT_ADALN) {
+    lrow = crow = (unsigned)((64ull * u0 + (unsigned)lane) / (unsigned)a.nb);
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      opa[c] = 1.0f;
+      sh[c] = -0.0f;
+    }
+    // the first unit's sample, before the unit loads go out (a later wait
+    // for these vectors then drains nothing but them)
+    if (crow < (unsigned)a.T) load_mod(a.tps >= a.T ? 0 : (int)(crow / (unsigned)a.tps));
+  }
+  const auto rst = rsrc_uniform(a.stats, FRONT == FRONT_ADALN && a.stats ? (int64_t)a.T * 8 : 0);
+  u32x2 pst[kDepth];  // ADALN: (mean, rstd) of the rows of the units in flight
+
   // ---- wave-uniform cursors: the next unit to load, the unit being stored
   const int64_t lstep = (int64_t)ustep * kUnitBytes;
   const uint8_t* lx = reinterpret_cast<const uint8_t*>(a.X) + (int64_t)u0 * kUnitBytes;
@@ -217,6 +295,11 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       pre[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(1024 * i + 16 * lane), 0, kNT);
+    if constexpr (FRONT == FRONT_ADALN) {
+      // rows past the end (the last unit's tail) read zeros
+      pst[slot] = __builtin_amdgcn_raw_buffer_load_b64(rst, lrow < (unsigned)a.T ? 8 * lrow : kOut, 0, 0);
+      lrow += (unsigned)a.rows_step;
+    }
     lx += lstep;
     lleft -= lstep;
   };
@@ -228,6 +311,7 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<u32x4*>(stage + 16 * chunk_pos(16 * i + (lane >> 2), lane & 3)) = pre[slot][i];
+    const u32x2 cst = FRONT == FRONT_ADALN ? pst[slot] : u32x2{0u, 0u};  // this unit's row statistics
     load(slot);  // the slot is free again: the loads of unit + kDepth go out now
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -237,19 +321,41 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
     float y[32];
     unsigned byte;
     u32x4 cw;
+    float mean = 0.0f, rstd = 1.0f;  // ADALN: this block's row statistics
     if constexpr (FRONT == FRONT_PROBE) {
       cw = w[0] ^ w[1] ^ w[2] ^ w[3];
       byte = cw[0] & 0xFFu;
     } else {
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          y[8 * qq + 2 * e] = bf16_lo(w[qq][e]);
-          y[8 * qq + 2 * e + 1] = bf16_hi(w[qq][e]);
+      if constexpr (FRONT == FRONT_ADALN) {
+        // a new sample for some lane: those lanes load its (1 + scale, shift)
+        // (a few times per wave at most; rows past the end keep theirs)
+        const bool live = crow < (unsigned)a.T;
+        const int smp = a.tps >= a.T ? 0 : (int)(crow / (unsigned)a.tps);
+        const bool chg = live && smp != cur_s;
+        if (__builtin_amdgcn_ballot_w64(chg) != 0) {
+          if (chg) load_mod(smp);
+          // wait here, on this rare path, so that no use of the vectors on
+          // the common path waits for them (such a wait would also drain the
+          // next units' loads, which are older than nothing)
+          __builtin_amdgcn_s_waitcnt(0);
         }
+        if (a.stats) {  // uniform
+          mean = __uint_as_float(cst[0]);
+          rstd = __uint_as_float(cst[1]);
+        }
+        modulate32(w, mean, rstd, opa, sh, y, nullptr);
+        crow += (unsigned)a.rows_step;
+      } else {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            y[8 * qq + 2 * e] = bf16_lo(w[qq][e]);
+            y[8 * qq + 2 * e + 1] = bf16_hi(w[qq][e]);
+          }
+      }
 
-      if constexpr (FRONT == FRONT_KRON) {
+      if constexpr (kKron) {
 #pragma unroll
         for (int k = 4; k >= 0; --k) {  // G5 (bit 0) first; the stages of different bits commute
           const int bit = 1 << (4 - k);
@@ -291,9 +397,21 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
         const bool near = near_pow2(amax);
         const uint64_t nearm = __builtin_amdgcn_ballot_w64(near);
         if (__builtin_expect(nearm != 0, 0)) {
+          if constexpr (FRONT == FRONT_ADALN) {
+            // the exact path reads its block from the stage: every lane
+            // writes its modulated bf16 values back there first
+            u32x4 x[4], mw[4];
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) x[qq] = *reinterpret_cast<const u32x4*>(stage + 16 * chunk_pos(lane, qq));
+            modulate32(x, mean, rstd, opa, sh, y, mw);
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) *reinterpret_cast<u32x4*>(stage + 16 * chunk_pos(lane, qq)) = mw[qq];
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+          }
           for (uint64_t m = nearm; m; m &= m - 1) {
             const int L = __builtin_ctzll(m);
-            exact_block<FRONT>(stage, L, lds_p[FRONT == FRONT_KRON ? wv : 0][L], lane, lds_res[wv][L],
+            exact_block<kKron ? FRONT_KRON : FRONT>(stage, L, lds_p[kKron ? wv : 0][L], lane, lds_res[wv][L],
                                STORE_Y ? lds_ys[STORE_Y ? wv : 0] : nullptr);
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -364,6 +482,10 @@ hipError_t launch_flat(int front, bool store_y, const FlatArgs& args, hipStream_
     case FRONT_SMOOTH: fn = pick<FRONT_SMOOTH>(store_y); break;
     case FRONT_HADAMARD: fn = pick<FRONT_HADAMARD>(store_y); break;
     case FRONT_PROBE: fn = (const void*)&flat_kernel<FRONT_PROBE, false>; break;
+    case FRONT_ADALN:
+      if (store_y) return hipErrorInvalidValue;
+      fn = (const void*)&flat_kernel<FRONT_ADALN, false>;
+      break;
     default: return hipErrorInvalidValue;
   }
   FlatArgs a = args;
@@ -378,6 +500,8 @@ hipError_t launch_flat(int front, bool store_y, const FlatArgs& args, hipStream_
   if (chunks > per_phase) chunks = per_phase;
   if (chunks < 1) chunks = 1;
   a.chunks = (int)chunks;
+  // a wave's units are phases x chunks units = chunks x 64 / gcd(64, nb) rows apart
+  a.rows_step = (int)(chunks * (64 / gcd64(a.nb)));
   const int64_t waves = (int64_t)a.phases * a.chunks;
   void* kargs[] = {&a};
   return hipLaunchKernel(fn, dim3((unsigned)((waves + kWaves - 1) / kWaves)), dim3(64 * kWaves), kargs, 0, stream);

@@ -74,8 +74,15 @@ struct FlatArgs {
   uint8_t* codes;
   uint8_t* scales;
   float* Y;
+  // FRONT_ADALN: per-row (mean, rstd) [T][2] (null: 0, 1), (1 + scale) and shift vectors
+  // [samples][d] (null: scale 0, shift -0), rows per sample (>= T: one sample)
+  const float* stats = nullptr;
+  const float* mscale = nullptr;
+  const float* mshift = nullptr;
+  int64_t tps = 0;
   int64_t nblocks, xbytes, units;
   int phases, chunks;
+  int rows_step;      // set by launch_flat: rows between a lane's consecutive blocks
   int req_waves = 0;  // requested total waves (tuning; 0: one resident round)
 };
 
