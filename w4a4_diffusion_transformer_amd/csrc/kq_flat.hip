@@ -126,13 +126,15 @@ __device__ __forceinline__ void modulate32(const u32x4 x[4], float mean, float r
 // block's 15 scalars p15 (kept in LDS by the kernel's setup; the quotients
 // 1/a are formed here, so that the common path carries no fp64 division).
 // The block is then quantized from these values: res receives its four code
-// words and its scale byte, ys (if not null) the 32 values.  Everything after the first
-// reads runs in registers, so that a wave meeting such a block is held up
-// only briefly.  Not inlined: the kernel's register allocation stays that of
-// its common path.
+// words and its scale byte, ys (if not null) the 32 values.  Everything after
+// the first reads runs in registers, so that a wave meeting such a block is
+// held up only briefly.  The KroQuant fronts inline it (as a call it cost
+// the kernel 20 more registers, 156 against 136, and 0.5-2% of its time);
+// the Hadamard front calls it (inlined there, up to 5% slower at the small
+// matrices).
 template <int FRONT>
-__device__ __attribute__((noinline)) void exact_block(const uint8_t* stage, int b, const float* p15, int lane,
-                                                      unsigned* res, float* ys) {
+__device__ __forceinline__ void exact_block(const uint8_t* stage, int b, const float* p15, int lane,
+                                            unsigned* res, float* ys) {
   const int c = lane & 31;
   u32x4 w[4];
 #pragma unroll
@@ -172,6 +174,12 @@ __device__ __attribute__((noinline)) void exact_block(const uint8_t* stage, int 
   if (lane < 32 && !(c & 1)) reinterpret_cast<uint8_t*>(res)[c >> 1] = (uint8_t)pair;
   if (lane == 0) res[4] = byte;
   if (ys && lane < 32) ys[c] = y;
+}
+
+template <int FRONT>
+__device__ __attribute__((noinline)) void exact_block_call(const uint8_t* stage, int b, const float* p15, int lane,
+                                                           unsigned* res, float* ys) {
+  exact_block<FRONT>(stage, b, p15, lane, res, ys);
 }
 
 template <int FRONT, bool STORE_Y>
@@ -411,8 +419,12 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
           }
           for (uint64_t m = nearm; m; m &= m - 1) {
             const int L = __builtin_ctzll(m);
-            exact_block<kKron ? FRONT_KRON : FRONT>(stage, L, lds_p[kKron ? wv : 0][L], lane, lds_res[wv][L],
-                               STORE_Y ? lds_ys[STORE_Y ? wv : 0] : nullptr);
+            if constexpr (kKron)
+              exact_block<FRONT_KRON>(stage, L, lds_p[wv][L], lane, lds_res[wv][L],
+                                      STORE_Y ? lds_ys[STORE_Y ? wv : 0] : nullptr);
+            else
+              exact_block_call<FRONT>(stage, L, lds_p[0][L], lane, lds_res[wv][L],
+                                      STORE_Y ? lds_ys[STORE_Y ? wv : 0] : nullptr);
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             __builtin_amdgcn_wave_barrier();
             if constexpr (STORE_Y) {
