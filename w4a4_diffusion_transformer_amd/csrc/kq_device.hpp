@@ -265,12 +265,15 @@ __device__ __forceinline__ void settle(float y[8], float amax, const uint16_t* _
 
 __device__ __forceinline__ unsigned e8m0_byte(float amax) {
   const unsigned ex = __float_as_uint(amax) >> 23;
-  return ex > 2u ? ex - 2u : 0u;
+  return __builtin_elementwise_sub_sat(ex, 2u);  // max(ex - 2, 0): one clamped subtract
 }
 
 __device__ __forceinline__ unsigned pack_fp4(const float y[8], unsigned byte) {
   const float scale = __uint_as_float(byte << 23);
-  unsigned w = 0;
+  // Each convert writes one byte of w and keeps the other three; the four
+  // together write all of them, so w may start from any value: y[0]'s bits
+  // (dead after this call on the common path) spare a register clear.
+  unsigned w = __float_as_uint(y[0]);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], scale, 0);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], scale, 1);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], scale, 2);

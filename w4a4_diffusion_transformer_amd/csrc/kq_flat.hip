@@ -53,16 +53,17 @@ constexpr int kUnitCodes = 64 * 16;   // code bytes of a unit
 // both touch every 4-byte bank of a 256-byte line once.
 __device__ __forceinline__ int chunk_pos(int b, int qq) { return 4 * b + (qq ^ ((b >> 2) & 3)); }
 
+// Two chains of three-input maxima (v_max3_f32 with |.| on its inputs): 16
+// instructions for the 32 values.
 __device__ __forceinline__ float absmax32(const float y[32]) {
-  float m0 = fabsf(y[0]), m1 = fabsf(y[1]), m2 = fabsf(y[2]), m3 = fabsf(y[3]);
+  float m0 = fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fabsf(y[2]));
+  float m1 = fmaxf(fmaxf(fabsf(y[16]), fabsf(y[17])), fabsf(y[18]));
 #pragma unroll
-  for (int c = 4; c < 32; c += 8) {
-    m0 = fmaxf(m0, fmaxf(fabsf(y[c]), fabsf(y[c + 4])));
-    m1 = fmaxf(m1, fmaxf(fabsf(y[c + 1]), fabsf(y[c + 5])));
-    m2 = fmaxf(m2, fmaxf(fabsf(y[c + 2]), fabsf(y[c + 6])));
-    m3 = fmaxf(m3, fmaxf(fabsf(y[c + 3]), fabsf(y[c + 7])));
-  }
-  return fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+  for (int c = 3; c < 15; c += 2) m0 = fmaxf(fmaxf(m0, fabsf(y[c])), fabsf(y[c + 1]));
+#pragma unroll
+  for (int c = 19; c < 31; c += 2) m1 = fmaxf(fmaxf(m1, fabsf(y[c])), fabsf(y[c + 1]));
+  m0 = fmaxf(fmaxf(m0, fabsf(y[15])), fabsf(y[31]));
+  return fmaxf(m0, m1);
 }
 
 // Maximum over the 32 lanes of each half of the wave (DPP within rows of
@@ -398,48 +399,53 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq) cw[qq] = pack_fp4(&y[8 * qq], byte);
       if constexpr (kSum) {
-        if (amax == 0.0f) cw = u32x4{0u, 0u, 0u, 0u};  // an all-zero block of a sum gives +0 codes
-        // Blocks whose amax is within 2^-16 of a power of two are quantized
-        // again from exact values, one at a time by the whole wave, after the
-        // packing above (so that y need not stay in registers along this path).
+        // Two rare cases share one test on the common path.  An all-zero
+        // block of a sum gives +0 codes (its values may be -0).  Blocks whose
+        // amax is within 2^-16 of a power of two are quantized again from
+        // exact values, one at a time by the whole wave, after the packing
+        // above (so that y need not stay in registers along this path).
+        const bool zero = amax == 0.0f;
         const bool near = near_pow2(amax);
-        const uint64_t nearm = __builtin_amdgcn_ballot_w64(near);
-        if (__builtin_expect(nearm != 0, 0)) {
-          if constexpr (FRONT == FRONT_ADALN) {
-            // the exact path reads its block from the stage: every lane
-            // writes its modulated bf16 values back there first
-            u32x4 x[4], mw[4];
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(zero || near) != 0, 0)) {
+          if (zero) cw = u32x4{0u, 0u, 0u, 0u};
+          const uint64_t nearm = __builtin_amdgcn_ballot_w64(near);
+          if (nearm != 0) {
+            if constexpr (FRONT == FRONT_ADALN) {
+              // the exact path reads its block from the stage: every lane
+              // writes its modulated bf16 values back there first
+              u32x4 x[4], mw[4];
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) x[qq] = *reinterpret_cast<const u32x4*>(stage + 16 * chunk_pos(lane, qq));
-            modulate32(x, mean, rstd, opa, sh, y, mw);
+              for (int qq = 0; qq < 4; ++qq) x[qq] = *reinterpret_cast<const u32x4*>(stage + 16 * chunk_pos(lane, qq));
+              modulate32(x, mean, rstd, opa, sh, y, mw);
 #pragma unroll
-            for (int qq = 0; qq < 4; ++qq) *reinterpret_cast<u32x4*>(stage + 16 * chunk_pos(lane, qq)) = mw[qq];
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-          }
-          for (uint64_t m = nearm; m; m &= m - 1) {
-            const int L = __builtin_ctzll(m);
-            if constexpr (kKron)
-              exact_block<FRONT_KRON>(stage, L, lds_p[wv][L], lane, lds_res[wv][L],
-                                      STORE_Y ? lds_ys[STORE_Y ? wv : 0] : nullptr);
-            else
-              exact_block_call<FRONT>(stage, L, lds_p[0][L], lane, lds_res[wv][L],
-                                      STORE_Y ? lds_ys[STORE_Y ? wv : 0] : nullptr);
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            if constexpr (STORE_Y) {
-              if (lane == L) {
-#pragma unroll
-                for (int c = 0; c < 32; ++c) y[c] = lds_ys[wv][c];
-              }
+              for (int qq = 0; qq < 4; ++qq) *reinterpret_cast<u32x4*>(stage + 16 * chunk_pos(lane, qq)) = mw[qq];
               __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
               __builtin_amdgcn_wave_barrier();
             }
-          }
-          if (near) {
-            const unsigned* r = lds_res[wv][lane];
-            cw = u32x4{r[0], r[1], r[2], r[3]};
-            byte = r[4];
+            for (uint64_t m = nearm; m; m &= m - 1) {
+              const int L = __builtin_ctzll(m);
+              if constexpr (kKron)
+                exact_block<FRONT_KRON>(stage, L, lds_p[wv][L], lane, lds_res[wv][L],
+                                        STORE_Y ? lds_ys[STORE_Y ? wv : 0] : nullptr);
+              else
+                exact_block_call<FRONT>(stage, L, lds_p[0][L], lane, lds_res[wv][L],
+                                        STORE_Y ? lds_ys[STORE_Y ? wv : 0] : nullptr);
+              __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+              __builtin_amdgcn_wave_barrier();
+              if constexpr (STORE_Y) {
+                if (lane == L) {
+#pragma unroll
+                  for (int c = 0; c < 32; ++c) y[c] = lds_ys[wv][c];
+                }
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+              }
+            }
+            if (near) {
+              const unsigned* r = lds_res[wv][lane];
+              cw = u32x4{r[0], r[1], r[2], r[3]};
+              byte = r[4];
+            }
           }
         }
       }
