@@ -126,11 +126,14 @@ __device__ __forceinline__ void modulate32(const u32x4 x[4], float mean, float r
 // rounded to fp32, with G = [[a, b], [l a, l b + 1/a]] in fp64 from the
 // block's 15 scalars p15 (kept in LDS by the kernel's setup; the quotients
 // 1/a are formed here, so that the common path carries no fp64 division).
+// The 32 products of a column are summed in one dependent chain, which sets
+// most of this path's time: splitting the products between the two
+// half-waves (fewer fp64 instructions, same chain) was no faster.
 // The block is then quantized from these values: res receives its four code
 // words and its scale byte, ys (if not null) the 32 values.  Everything after
 // the first reads runs in registers, so that a wave meeting such a block is
 // held up only briefly.  The KroQuant fronts inline it (as a call it cost
-// the kernel 20 more registers, 156 against 136, and 0.5-2% of its time);
+// the kernel 20 more registers and 0.5-2% of its time);
 // the Hadamard front calls it (inlined there, up to 5% slower at the small
 // matrices).
 template <int FRONT>
@@ -146,13 +149,25 @@ __device__ __forceinline__ void exact_block(const uint8_t* stage, int b, const f
   };
   double s = 0.0;
   if constexpr (FRONT == FRONT_KRON) {
+    // Lane k < 5 forms the two computed entries of factor k, l a and
+    // l b + 1/a (l b is exact in fp64: one rounding), so that the wave runs
+    // one fp64 division instead of five; every lane then takes the entries
+    // of its column c from lanes 0 .. 4.
+    const int kk = lane < 5 ? lane : 0;
+    const double Lk = p15[3 * kk], Ak = p15[3 * kk + 1], Bk = p15[3 * kk + 2];
+    const double q0 = Lk * Ak, q1 = fma(Lk, Bk, 1.0 / Ak);
+    auto from_lane = [](double v, int k) {
+      const uint64_t u = __builtin_bit_cast(uint64_t, v);
+      const unsigned lo = __builtin_amdgcn_readlane((unsigned)u, k);
+      const unsigned hi = __builtin_amdgcn_readlane((unsigned)(u >> 32), k);
+      return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+    };
     double e0[5], e1[5];  // entries G_k[0][bit] and G_k[1][bit] of column c's bit of each factor
 #pragma unroll
     for (int k = 0; k < 5; ++k) {
-      const double L = p15[3 * k], A = p15[3 * k + 1], B = p15[3 * k + 2];
       const bool bit = (c >> (4 - k)) & 1;
-      e0[k] = bit ? B : A;
-      e1[k] = bit ? fma(L, B, 1.0 / A) : L * A;  // l b is exact in fp64: one rounding, as l b + 1/a
+      e0[k] = (double)(bit ? p15[3 * k + 2] : p15[3 * k + 1]);
+      e1[k] = bit ? from_lane(q1, k) : from_lane(q0, k);
     }
 #pragma unroll
     for (int r = 0; r < 32; ++r) {
