@@ -38,8 +38,19 @@ constexpr int kRT = 2;                             // 16-row MFMA sub-tiles per 
 constexpr int kRows = 16 * kRT;                    // rows per tile
 constexpr int kPieces = kRows * kCB * 4;           // 16-byte pieces of X per tile
 constexpr int kPPT = kPieces / kThreads;           // pieces per thread per tile
-constexpr int kInStride = kCB * 64 + 16;           // LDS bytes per input row (16 B pad: conflict-free reads)
-constexpr int kOutStride = kCB * 16 + 16;          // LDS bytes per code row (stride 4 mod 64 dwords)
+// LDS bytes per input row: 528 = 132 dwords, 4 banks apart mod 64, so the
+// block reads (16 lanes on 16 rows, 16 bytes each) touch every bank once.
+constexpr int kInStride = kCB * 64 + 16;
+// LDS bytes per code row: 144 = 36 dwords.  The 4-byte code writes (16 rows
+// x 4 lanes) touch every bank once; the 16-byte reads of the row segments
+// (8 lanes on each of two rows) do not: the two rows' 32-dword spans start
+// 36 dwords apart and share banks 0-3 mod 64.  The counters show bank
+// conflicts for this kernel (about 1.5 cycles per LDS instruction), none
+// for the block-per-lane kernel.  A dense 128-byte row with the chunk index
+// XOR-swizzled by row pair (both accesses then touch every bank once)
+// removed a quarter of those cycles and changed no timing: the rest come
+// from elsewhere, and none of them is on the kernel's critical path.
+constexpr int kOutStride = kCB * 16 + 16;
 constexpr int kInBytes = kRows * kInStride;
 constexpr int kOutBytes = kRows * kOutStride;
 constexpr int kScaleBytes = kRows * kCB;
