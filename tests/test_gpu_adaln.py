@@ -182,6 +182,21 @@ def test_fused_full_workloads(name, T, d, tps, kind, variant):
     check(f"adaln {name} v{variant}", X, P, st, sc, sh, tps, variant)
 
 
+@pytest.mark.parametrize("T,d,tps", [
+    (4096, 2240, 32),    # 128 samples: every wave's run of units crosses many sample boundaries
+    (2048, 3072, 96),    # 22 samples of 96 rows, the last one short
+    (1536, 1152, 1504),  # two samples, the boundary inside a unit (36 blocks per row)
+    (1000, 160, 64),     # 5 blocks per row (phases of 5 units; units span 12.8 rows)
+])
+def test_fused_sample_boundaries(T, d, tps):
+    """Batches of several samples: the default kernel gives each wave a
+    contiguous band of rows and loads the vectors of the band's first sample
+    for the whole workgroup; lanes whose rows lie in a later sample load
+    their own.  Every case against the oracle's producer step + quantizer."""
+    X, P, st, sc, sh = inputs(T, d, tps, seed=T + d + tps)
+    check(f"adaln {T}x{d} tps{tps} boundaries", X, P, st, sc, sh, tps, 3)
+
+
 def test_modulation_vectors_at_an_offset():
     """Modulation vectors passed as views 16 bytes into larger buffers (the
     alignment the entry point requires) give the same bytes as contiguous ones;

@@ -8,13 +8,15 @@
 // back so that lane i holds all 32 channels of block i of the unit.  The
 // whole transform, the block amax, the E8M0 byte and the E2M1 codes then
 // stay inside one lane, and the lane's 16 code bytes and its scale byte are
-// stored as one contiguous 1 KB + 64 B per wave.  No workgroup barrier: the
-// waves of a workgroup never share data.
+// stored as one contiguous 1 KB + 64 B per wave.  The waves of a workgroup
+// never share unit data; only FRONT_ADALN shares its modulation vectors,
+// once, at setup.
 //
 // A wave visits units u0, u0 + P C, u0 + 2 P C, ... with P = nb / gcd(64, nb)
 // units spanning a whole number of rows, so lane i always holds the same
 // block column j = (64 u0 + i) mod nb and keeps that block's coefficients in
-// registers for all of its units.
+// registers for all of its units.  (FRONT_ADALN on a batch of several
+// samples: u0, u0 + P, u0 + 2P, ..., a contiguous band of rows.)
 //
 // FRONT_KRON: y = x K(j), K = G1 (x) ... (x) G5 (KroQuant; Pith review,
 // "What carries the argument": the on-the-fly kernel that builds each block
@@ -209,18 +211,58 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
 
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // consecutive waves take consecutive phases (the four waves of a
-  // workgroup stream adjacent units); unit indices stay below 2^29
-  // (tokens * d < 2^40), so the index arithmetic is 32-bit
-  const unsigned gw = (unsigned)__builtin_amdgcn_readfirstlane((int)blockIdx.x * kWaves + wv);
   const unsigned nph = (unsigned)a.phases;
-  if (gw >= nph * (unsigned)a.chunks) return;  // wave-uniform; nothing below synchronizes the workgroup
-  const int ph = (int)(gw % nph), chk = (int)(gw / nph);
-  const unsigned u0 = (unsigned)ph + (unsigned)a.phases * (unsigned)chk;  // first unit
-  const unsigned ustep = (unsigned)a.phases * (unsigned)a.chunks;        // units between this wave's units
   const unsigned units = (unsigned)a.units;
-  if (u0 >= units) return;
-  const int n = (int)((units - 1 - u0) / ustep) + 1;
+  // Wave -> (phase, chunk); unit indices stay below 2^29 (tokens * d <
+  // 2^40), so the index arithmetic is 32-bit.  Most fronts: consecutive
+  // waves take consecutive phases (the four waves of a workgroup stream
+  // adjacent units), and no wave waits for another.  ADALN: the four waves
+  // of a workgroup share one phase (consecutive chunks), so that they share
+  // one copy of the modulation vectors of its 64 block columns (two
+  // workgroup barriers at setup, which a wave without units joins too).
+  int ph, chk, n;
+  unsigned u0, ustep;
+  unsigned wg_u0 = 0;  // ADALN: first unit of the workgroup's wave 0 (units if it has none)
+  const bool contiguous = FRONT == FRONT_ADALN && a.tps < a.T;  // uniform
+  if constexpr (FRONT == FRONT_ADALN) {
+    ph = (int)(blockIdx.x % nph);
+    chk = (int)(blockIdx.x / nph) * kWaves + wv;
+    if ((unsigned)ph >= units) return;  // uniform over the workgroup
+    // This wave's units: u0, u0 + ustep, ... (n of them).  Several samples:
+    // a contiguous run of the phase's units, so that a wave's rows seldom
+    // change sample.  One sample: chunk c of the phase starts at unit
+    // ph + P c and steps over the whole resident round.  A chunk past the
+    // last has no units and starts at unit `units` (its loads fetch nothing).
+    auto run_start = [&](unsigned c, int& cnt_out) -> unsigned {
+      const unsigned C = (unsigned)a.chunks;
+      if (c >= C) {
+        cnt_out = 0;
+        return units;
+      }
+      if (contiguous) {
+        const unsigned cnt = (units - 1 - (unsigned)ph) / nph + 1;
+        const unsigned cq = cnt / C, cr = cnt % C;
+        cnt_out = (int)(cq + (c < cr ? 1u : 0u));
+        return cnt_out ? (unsigned)ph + nph * (c * cq + (c < cr ? c : cr)) : units;
+      }
+      const unsigned u = (unsigned)ph + nph * c;
+      cnt_out = u < units ? (int)((units - 1 - u) / (nph * C)) + 1 : 0;
+      return cnt_out ? u : units;
+    };
+    u0 = run_start((unsigned)chk, n);
+    ustep = contiguous ? nph : nph * (unsigned)a.chunks;
+    int cnt0;
+    wg_u0 = run_start((unsigned)(chk - wv), cnt0);
+  } else {
+    const unsigned gw = (unsigned)__builtin_amdgcn_readfirstlane((int)blockIdx.x * kWaves + wv);
+    if (gw >= nph * (unsigned)a.chunks) return;  // wave-uniform; nothing below synchronizes the workgroup
+    ph = (int)(gw % nph);
+    chk = (int)(gw / nph);
+    u0 = (unsigned)ph + (unsigned)a.phases * (unsigned)chk;  // first unit
+    ustep = (unsigned)a.phases * (unsigned)a.chunks;         // units between this wave's units
+    if (u0 >= units) return;
+    n = (int)((units - 1 - u0) / ustep) + 1;
+  }
   // this lane's block column, for every unit: (64 ph + lane) mod nb
   const unsigned nb = (unsigned)a.nb;
   const unsigned j0 = (64u * (unsigned)ph) % nb;  // wave-uniform
@@ -294,6 +336,8 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
     }
     cur_s = smp;
   };
+  f32x4 mq[4];  // ADALN: this wave's quarter of the workgroup's (scale, shift) slices, as loaded
+  int smp0 = 0;
   if constexpr (FRONT == FRONT_ADALN) {
     lrow = crow = (unsigned)((64ull * u0 + (unsigned)lane) / (unsigned)a.nb);
 #pragma unroll
@@ -301,9 +345,23 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
       opa[c] = 1.0f;
       sh[c] = -0.0f;
     }
-    // the first unit's sample, before the unit loads go out (a later wait
-    // for these vectors then drains nothing but them)
-    if (crow < (unsigned)a.T) load_mod(a.tps >= a.T ? 0 : (int)(crow / (unsigned)a.tps));
+    // The sample of the workgroup's first row, for every lane of its four
+    // waves: the (scale, shift) slices of the phase's 64 block columns, read
+    // with coalesced loads (eight 128-byte slices per instruction, a quarter
+    // of them by each wave) before the unit loads go out, and passed to
+    // their lanes through the workgroup's stages after.  Lanes whose rows
+    // lie in another sample load their own when they reach them.
+    if (contiguous && wg_u0 < units) smp0 = (int)((64ull * wg_u0 / nb) / (unsigned)a.tps);
+    const float* src = wv < 2 ? a.mscale : a.mshift;  // wave-uniform
+    if (src) {
+      const int64_t base = (int64_t)smp0 * (32 * (int64_t)a.nb);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const unsigned bo = 32u * (unsigned)(wv & 1) + 8u * (unsigned)i + ((unsigned)lane >> 3);
+        mq[i] = *reinterpret_cast<const f32x4*>(src + base + 32 * (int64_t)((j0 + bo) % nb) + 4 * (lane & 7));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
   const auto rst = rsrc_uniform(a.stats, FRONT == FRONT_ADALN && a.stats ? (int64_t)a.T * 8 : 0);
   u32x2 pst[kDepth];  // ADALN: (mean, rstd) of the rows of the units in flight
@@ -487,6 +545,40 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
     load(s);
     __builtin_amdgcn_sched_barrier(0);
   }
+  if constexpr (FRONT == FRONT_ADALN) {
+    // The slices to their lanes through the four stages (16 KB, free until
+    // the first unit): piece q (16 bytes) of slice b of vector t (scale,
+    // shift) at piece 512 t + 8 b + (q ^ ((b >> 1) & 7)), XOR-swizzled by
+    // slice pair so that the writes (two slices per 16 lanes) and the reads
+    // (16 slices per 16 lanes) touch every bank once.
+    uint8_t* mods = &lds_x[0][0];
+    if (wv < 2 ? a.mscale != nullptr : a.mshift != nullptr) {  // wave-uniform
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int bo = 32 * (wv & 1) + 8 * i + (lane >> 3), q = lane & 7;
+        *reinterpret_cast<f32x4*>(mods + 16 * (512 * (wv >> 1) + 8 * bo + (q ^ ((bo >> 1) & 7)))) = mq[i];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (t == 0 ? a.mscale == nullptr : a.mshift == nullptr) continue;  // uniform
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const f32x4 r = *reinterpret_cast<const f32x4*>(mods + 16 * (512 * t + 8 * lane + (q ^ ((lane >> 1) & 7))));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (t == 0)
+            opa[4 * q + e] = 1.0f + r[e];
+          else
+            sh[4 * q + e] = r[e];
+        }
+      }
+    }
+    cur_s = smp0;
+    __syncthreads();  // every wave holds its vectors before any stage takes a unit
+    if (n == 0) return;
+  }
   for (int k0 = 0; k0 < n; k0 += kDepth) {
 #pragma unroll
     for (int s = 0; s < kDepth; ++s)
@@ -530,14 +622,19 @@ hipError_t launch_flat(int front, bool store_y, const FlatArgs& args, hipStream_
   // one resident round of waves: every wave then owns about the same number of units
   const int64_t slots = (int64_t)cu_count() * resident_per_cu(fn, 64 * kWaves) * kWaves;
   int64_t chunks = a.req_waves > 0 ? (int64_t)a.req_waves / a.phases : slots / a.phases;
+  const bool adaln = front == FRONT_ADALN;
+  if (adaln && chunks >= kWaves) chunks -= chunks % kWaves;  // whole workgroups per phase
   if (chunks > per_phase) chunks = per_phase;
   if (chunks < 1) chunks = 1;
   a.chunks = (int)chunks;
-  // a wave's units are phases x chunks units = chunks x 64 / gcd(64, nb) rows apart
-  a.rows_step = (int)(chunks * (64 / gcd64(a.nb)));
-  const int64_t waves = (int64_t)a.phases * a.chunks;
+  // consecutive units of a wave are phases x chunks units = chunks x 64 / gcd(64, nb) rows
+  // apart, or phases units = 64 / gcd(64, nb) rows for a contiguous run (ADALN, several samples)
+  a.rows_step = (int)((adaln && a.tps < a.T ? 1 : chunks) * (64 / gcd64(a.nb)));
+  // ADALN: a workgroup per phase and four chunks; otherwise four consecutive waves
+  const int64_t groups = adaln ? a.phases * ((chunks + kWaves - 1) / kWaves)
+                               : (a.phases * chunks + kWaves - 1) / kWaves;
   void* kargs[] = {&a};
-  return hipLaunchKernel(fn, dim3((unsigned)((waves + kWaves - 1) / kWaves)), dim3(64 * kWaves), kargs, 0, stream);
+  return hipLaunchKernel(fn, dim3((unsigned)groups), dim3(64 * kWaves), kargs, 0, stream);
 }
 
 }  // namespace kq
