@@ -43,6 +43,13 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def sha256_of(a) -> str:
+    """SHA-256 of a host buffer's bytes (inputs are reported by hash, so that a
+    run can be matched to the buffers it measured)."""
+    import numpy as np
+    return hashlib.sha256(np.ascontiguousarray(a).view(np.uint8).tobytes()).hexdigest()
+
+
 def load_profile(kernel: str, workload: str) -> dict:
     """HBM bytes per launch (rocprofv3 counters) and the kernel-trace average of
     the committed summaries, if they were taken on the current kernel sources."""
@@ -153,7 +160,8 @@ def shape_table(kq, torch, np, synth, dev):
             calls["smoothquant"] = (L.kq_smooth_quantize, lambda i: (xs[i], T, d, mp, *os_[i], stream))
             calls["plain"] = (L.kq_mx_quantize, lambda i: (xs[i], T, d, *os_[i], stream))
             calls["hadamard32"] = (L.kq_hadamard_quantize, lambda i: (xs[i], T, d, *os_[i], stream))
-        row = {"T": T, "d": d, "auto_variant": kq.variant_name(kq.kq_auto_variant(T, d, True, False))}
+        row = {"T": T, "d": d, "auto_variant": kq.variant_name(kq.kq_auto_variant(T, d, True, False)),
+               "X_sha256": sha256_of(X), "params_sha256": sha256_of(P)}
         if not spec.shared_k:
             # kq_tune's record for this shape (K_params and the dense split both supplied), then
             # timed through KQ_AUTO on the cold copies
@@ -263,7 +271,8 @@ def adaln_table(kq, torch, np, synth, dev):
             xm = ((Xs[i].view(torch.bfloat16).float() - st[:, :1]) * st[:, 1:] * (1.0 + rep_sc) + rep_sh).to(torch.bfloat16)
             return L.kq_quantize_ex(xm.data_ptr(), T, d, Pd.data_ptr(), 15, None, kq.KQ_AUTO, *ops[i], stream)
 
-        row = {"T": T, "d": d, "tokens_per_sample": tps}
+        row = {"T": T, "d": d, "tokens_per_sample": tps, "X_sha256": sha256_of(X), "params_sha256": sha256_of(P),
+               "scale_sha256": sha256_of(sc), "shift_sha256": sha256_of(sh)}
         for label, fn in (("fused_quantize_adaln", fused), ("fused_quantize_adaln_mfma_otf", fused_otf), ("row_stats", stats),
                           ("unfused_torch_eager_modulate_then_quantize", unfused)):
             secs = time_calls(torch, fn, [(i,) for i in range(copies)], max(60, 4 * copies))
@@ -445,6 +454,7 @@ def main():
     X = synth.matrix(spec)
     P = synth.params(spec)
     m = synth.smooth_mult(X)
+    x_sha, p_sha = sha256_of(X), sha256_of(P)
     print(f"# generated {T}x{d} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     Xs = [torch.from_numpy(X.view(np.int16)).to(dev)]
@@ -598,7 +608,11 @@ def main():
                                f"{CALLS} back-to-back kq_quantize calls per step",
                    "tokens": T, "d": d, "calls_per_step": CALLS, "variant": variant_name,
                    "gelem_per_s": round(n * CALLS * args.steps / (ms * 1e-3) / 1e9, 1),
-                   "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2)},
+                   "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+                   "X_sha256": x_sha, "params_sha256": p_sha},
+        "device": {"name": torch.cuda.get_device_name(0),
+                   "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", ""),
+                   "compute_units": torch.cuda.get_device_properties(0).multi_processor_count},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "comparison": comparison,
