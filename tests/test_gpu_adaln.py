@@ -132,6 +132,27 @@ def test_row_stats(T, d):
     assert (u == 0).mean() >= 0.99
 
 
+@pytest.mark.parametrize("d", [1152, 3072, 12288])
+def test_row_stats_offset_rows(d):
+    """Rows whose mean is large against their spread: the kernel takes
+    sum (x - mean)^2 as sum x^2 - mean sum x only while that stays accurate,
+    and these rows (mean^2 / var from about 1 to about 10^5) land on both
+    sides of that test, next to plain rows, in one launch."""
+    rng = np.random.default_rng(d)
+    T = 64
+    base = [(0.0, 1.0), (30.0, 1.0), (1000.0, 8.0), (-200.0, 0.5), (5.0, 0.05), (64.0, 2.0), (2.0, 1.0), (-1.0, 0.02)]
+    rows = [rng.normal(base[i % len(base)][0], base[i % len(base)][1], d).astype(np.float32) for i in range(T)]
+    X = synth.f32_to_bf16(np.stack(rows))
+    st = torch.empty((T, 2), dtype=torch.float32, device="cuda:0")
+    kq.kq_row_stats(dev(X), EPS, st)
+    torch.cuda.synchronize()
+    ref = oracle.row_stats(X, eps=EPS)
+    got = host(st)
+    u = ulp_diff(got, ref)
+    assert u.max() <= 1, f"max ulp {u.max()}"
+    assert (u == 0).mean() >= 0.99
+
+
 def test_row_stats_constant_and_zero_rows():
     X = np.zeros((4, 64), dtype=np.uint16)
     X[1] = synth.f32_to_bf16(np.full(64, 3.0, np.float32))
