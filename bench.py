@@ -511,6 +511,18 @@ def main():
             kq.kq_smooth_quantize(fx, fm, *fo)
             kq.kq_quantize_ex(fx, fp, 15, None, kq.KQ_MFMA_OTF, *fo)
             del fx, fo
+        # the AdaLN producer step at FLUX X1 (one sample) and PixArt X1 (two samples), the inputs of
+        # the adaln table: row statistics, then the fused quantizer (default kernel)
+        for at, ad, atps in ((4608, 3072, 4608), (8192, 1152, 4096)):
+            ax = torch.from_numpy(synth.random_matrix(at, ad, seed=41, n_outliers=ad // 100, mult=50.0,
+                                                      token_sigma=0.5).view(np.int16)).to(dev)
+            ap = torch.from_numpy(synth.random_params(ad // 32, seed=42)).to(dev)
+            asc, ash = synth.adaln_vectors((at + atps - 1) // atps, ad, seed=43)
+            ast = torch.empty((at, 2), dtype=torch.float32, device=dev)
+            ao = kq.alloc_outputs(ax)
+            kq.kq_row_stats(ax, 1e-6, ast)
+            kq.kq_quantize_adaln(ax, ast, torch.from_numpy(asc).to(dev), torch.from_numpy(ash).to(dev), atps, ap, *ao)
+            del ax, ao
         # the W4A4 GEMM once at the FLUX MLP fc1 shape
         gm, gn, gk = 4608, 12288, 3072
         ga = torch.randint(0, 256, (gm, gk // 2), dtype=torch.uint8, device=dev)

@@ -372,14 +372,21 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
   int64_t lleft = a.xbytes - (int64_t)u0 * kUnitBytes;  // bytes from the load cursor to the end of X
   auto clamp_bytes = [](int64_t left, int unit) { return left <= 0 ? 0 : (left >= unit ? unit : (int)left); };
   u32x4 pre[kDepth][4];
+  // The loads issued after a wave's last unit fetch nothing.  With the
+  // interleaved order they lie past the end of X; ADALN's contiguous runs
+  // would otherwise read the start of the next wave's run a second time, so
+  // that front counts its loads.
+  int loads_left = n;
   auto load = [&](int slot) {
-    const auto rx = rsrc_uniform(lx, clamp_bytes(lleft, kUnitBytes));
+    bool mine = true;
+    if constexpr (FRONT == FRONT_ADALN) mine = loads_left-- > 0;  // uniform
+    const auto rx = rsrc_uniform(lx, mine ? clamp_bytes(lleft, kUnitBytes) : 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       pre[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(rx, (uint32_t)(1024 * i + 16 * lane), 0, kNT);
     if constexpr (FRONT == FRONT_ADALN) {
       // rows past the end (the last unit's tail) read zeros
-      pst[slot] = __builtin_amdgcn_raw_buffer_load_b64(rst, lrow < (unsigned)a.T ? 8 * lrow : kOut, 0, 0);
+      pst[slot] = __builtin_amdgcn_raw_buffer_load_b64(rst, mine && lrow < (unsigned)a.T ? 8 * lrow : kOut, 0, 0);
       lrow += (unsigned)a.rows_step;
     }
     lx += lstep;
