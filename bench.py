@@ -225,7 +225,9 @@ def adaln_table(kq, torch, np, synth, dev):
     Unfused: a LayerNorm + modulation written as torch ops (fp32 math, one bf16
     tensor written back to HBM) followed by kq_quantize on that tensor.  Fused:
     kq_quantize_adaln on the raw activation with the row statistics.  The row
-    statistics kernel is timed on its own, and the fused step also on the MFMA kernel (mfma_otf).
+    statistics kernel is timed on its own and followed by the fused step on the
+    same X (as a pipeline runs them: the second read of X may come from the
+    Infinity Cache), and the fused step also on the MFMA kernel (mfma_otf).
     Inputs: FLUX.1-schnell width
     (one sample of 4608 tokens x 3072) and PixArt-Sigma width (2 x 4096 tokens
     x 1152), N(0,1) activations with 1% outlier channels, AdaLN vectors with 1%
@@ -266,6 +268,10 @@ def adaln_table(kq, torch, np, synth, dev):
         def stats(i):
             return L.kq_row_stats(xs[i], T, d, 1e-6, stp[i], stream)
 
+        def stats_then_fused(i):  # the producer step as a pipeline runs it: both kernels on one X
+            rc = L.kq_row_stats(xs[i], T, d, 1e-6, stp[i], stream)
+            return rc or fused(i)
+
         def unfused(i):
             st = sts[i]
             xm = ((Xs[i].view(torch.bfloat16).float() - st[:, :1]) * st[:, 1:] * (1.0 + rep_sc) + rep_sh).to(torch.bfloat16)
@@ -274,6 +280,7 @@ def adaln_table(kq, torch, np, synth, dev):
         row = {"T": T, "d": d, "tokens_per_sample": tps, "X_sha256": sha256_of(X), "params_sha256": sha256_of(P),
                "scale_sha256": sha256_of(sc), "shift_sha256": sha256_of(sh)}
         for label, fn in (("fused_quantize_adaln", fused), ("fused_quantize_adaln_mfma_otf", fused_otf), ("row_stats", stats),
+                          ("row_stats_then_fused_quantize_adaln", stats_then_fused),
                           ("unfused_torch_eager_modulate_then_quantize", unfused)):
             secs = time_calls(torch, fn, [(i,) for i in range(copies)], max(60, 4 * copies))
             sec = secs[len(secs) // 2]
