@@ -305,6 +305,7 @@ constexpr uint32_t kOut = 0xFFFFFFF0u;   // buffer offset past every range: load
 constexpr int kMaxRecords = 0x7FFFFFFF;  // range cap; in-range offsets stay below 32 d <= 2^29
 constexpr int kRsrcFlags = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family descriptor word 3)
 constexpr int kNT = 2;                   // cache-policy bit of a buffer access: non-temporal (streamed once)
+constexpr int kSC1 = 16;                 // cache-policy bit of a buffer access: device scope
 
 // Raw buffer descriptor over [base, base + bytes): loads at or past `bytes`
 // return zero and stores there are dropped (the hardware range check), so a

@@ -200,7 +200,9 @@ __device__ __attribute__((noinline)) void exact_block_call(const uint8_t* stage,
   exact_block<FRONT>(stage, b, p15, lane, res, ys);
 }
 
-template <int FRONT, bool STORE_Y>
+// CPOL: the cache policy of the code and scale stores (0, or kSC1: device
+// scope, below at launch_flat).
+template <int FRONT, bool STORE_Y, int CPOL>
 __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
   __shared__ __attribute__((aligned(256))) uint8_t lds_x[kWaves][kUnitBytes];
   constexpr bool kKron = FRONT == FRONT_KRON || FRONT == FRONT_ADALN;  // fronts with KroQuant's transform
@@ -532,8 +534,8 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
     }
     const auto rc = rsrc_uniform(a.codes + ub * 16, clamp_bytes(a.nblocks * 16 - ub * 16, kUnitCodes));
     const auto rs = rsrc_uniform(a.scales + ub, clamp_bytes(a.nblocks - ub, kUnitBlocks));
-    __builtin_amdgcn_raw_buffer_store_b128(cw, rc, (uint32_t)(16 * lane), 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)byte, rs, (uint32_t)lane, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(cw, rc, (uint32_t)(16 * lane), 0, CPOL);
+    __builtin_amdgcn_raw_buffer_store_b8((uint8_t)byte, rs, (uint32_t)lane, 0, CPOL);
     if constexpr (STORE_Y) {
       const auto ry = rsrc_uniform(a.Y + ub * 32, clamp_bytes((a.nblocks - ub) * 128, kUnitBlocks * 128));
 #pragma unroll
@@ -593,9 +595,10 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
   }
 }
 
-template <int FRONT>
+// The diagnostic form that also stores y keeps the default store policy.
+template <int FRONT, int CPOL>
 const void* pick(bool store_y) {
-  return store_y ? (const void*)&flat_kernel<FRONT, true> : (const void*)&flat_kernel<FRONT, false>;
+  return store_y ? (const void*)&flat_kernel<FRONT, true, 0> : (const void*)&flat_kernel<FRONT, false, CPOL>;
 }
 
 int gcd64(int nb) {
@@ -606,17 +609,27 @@ int gcd64(int nb) {
 
 }  // namespace
 
+// Store policy, measured on MI355X (same process, identical outputs):
+// device-scope stores take 2-7% off the fronts with arithmetic (KroQuant,
+// AdaLN, Hadamard) at every DiT matrix and 2% at 453 MB.  The fronts with
+// little or none (plain, SmoothQuant, probe) gain 2-5% with them from about
+// 64 MiB of X and lose 1-7% below, so they switch there.
+constexpr int64_t kScopeSwitchBytes = 64ll << 20;
+
 hipError_t launch_flat(int front, bool store_y, const FlatArgs& args, hipStream_t stream) {
   const void* fn = nullptr;
+  const bool big = (int64_t)args.T * args.nb * 64 >= kScopeSwitchBytes;
   switch (front) {
-    case FRONT_KRON: fn = pick<FRONT_KRON>(store_y); break;
-    case FRONT_PLAIN: fn = pick<FRONT_PLAIN>(store_y); break;
-    case FRONT_SMOOTH: fn = pick<FRONT_SMOOTH>(store_y); break;
-    case FRONT_HADAMARD: fn = pick<FRONT_HADAMARD>(store_y); break;
-    case FRONT_PROBE: fn = (const void*)&flat_kernel<FRONT_PROBE, false>; break;
+    case FRONT_KRON: fn = pick<FRONT_KRON, kSC1>(store_y); break;
+    case FRONT_PLAIN: fn = big ? pick<FRONT_PLAIN, kSC1>(store_y) : pick<FRONT_PLAIN, 0>(store_y); break;
+    case FRONT_SMOOTH: fn = big ? pick<FRONT_SMOOTH, kSC1>(store_y) : pick<FRONT_SMOOTH, 0>(store_y); break;
+    case FRONT_HADAMARD: fn = pick<FRONT_HADAMARD, kSC1>(store_y); break;
+    case FRONT_PROBE:
+      fn = big ? (const void*)&flat_kernel<FRONT_PROBE, false, kSC1> : (const void*)&flat_kernel<FRONT_PROBE, false, 0>;
+      break;
     case FRONT_ADALN:
       if (store_y) return hipErrorInvalidValue;
-      fn = (const void*)&flat_kernel<FRONT_ADALN, false>;
+      fn = (const void*)&flat_kernel<FRONT_ADALN, false, kSC1>;
       break;
     default: return hipErrorInvalidValue;
   }

@@ -299,7 +299,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int m0, int n0, uin
   __builtin_amdgcn_s_waitcnt(0x0070 | 0x0F00);
 
   // Y rows m0 + 32 MI wm + 32 i + 8 (r / 4) + 4 fh + r % 4, columns n0 + 64 wn + 32 j + fr; one
-  // descriptor per 32-row band (ranges stay far below 2^31 bytes for any N).
+  // descriptor per 32-row band (ranges stay far below 2^31 bytes for any N).  Device-scope
+  // stores: 1-9% faster than the default policy at the DiT shapes (MI355X), non-temporal ones
+  // no faster.
   const int64_t N = g.N;
 #pragma unroll
   for (int i = 0; i < MI; ++i) {
@@ -315,7 +317,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int m0, int n0, uin
         for (int r = 0; r < 16; ++r) {
           const int row = 8 * (r >> 2) + 4 * fh + (r & 3);
           const uint32_t off = col < nrows ? (uint32_t)((row * N + n0 + col) * 4) : kOut;
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), ry, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][r]), ry, off, 0, kSC1);
         }
       }
     }
@@ -329,7 +331,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int m0, int n0, uin
           const int row = 8 * (r >> 2) + 4 * fh + (r & 3);
           const uint32_t off = col < nrows ? (uint32_t)((row * N + n0 + col) * 2) : kOut;
           const __bf16 h = (__bf16)acc[i][j][r];
-          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, h), ry, off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, h), ry, off, 0, kSC1);
         }
       }
     }
