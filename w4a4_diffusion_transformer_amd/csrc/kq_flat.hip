@@ -93,9 +93,14 @@ __device__ __forceinline__ float max32(float v) {
 // absent input is an identity operand (mean +0, rstd 1, opa 1, sh -0), which
 // leaves v exactly x, signed zeros included.  y[c] receives the bf16 value
 // as fp32; w (if not null) the bf16 pairs, even channel in the low half.
+// The rounding converts the pair (+0, v): the bf16 lands in the high half of
+// a word whose low half is zero, so the word is already the fp32 value (one
+// convert per value and no shift back).
 __device__ __forceinline__ void modulate32(const u32x4 x[4], float mean, float rstd, const float opa[32],
                                            const float sh[32], float y[32], u32x4* w) {
 #pragma clang fp contract(off)
+  typedef __attribute__((ext_vector_type(2))) float f32x2;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 #pragma unroll
   for (int qq = 0; qq < 4; ++qq)
 #pragma unroll
@@ -109,10 +114,9 @@ __device__ __forceinline__ void modulate32(const u32x4 x[4], float mean, float r
         v = v * rstd;
         v = v * opa[c];
         v = v + sh[c];
-        const __bf16 b = (__bf16)v;
-        const unsigned bits = __builtin_bit_cast(unsigned short, b);
-        y[c] = __uint_as_float(bits << 16);
-        pair |= bits << (16 * h);
+        const unsigned word = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{0.0f, v}, bf16x2));
+        y[c] = __uint_as_float(word);
+        pair |= h ? word : word >> 16;
       }
       if (w) w[qq][e] = pair;
     }
