@@ -408,13 +408,14 @@ def test_error_codes_on_device_buffers():
     assert L.kq_quantize(X.data_ptr(), 4, 48, P.data_ptr(), codes.data_ptr(), scales.data_ptr(), None) == 2
 
 
-@pytest.mark.parametrize("T,d", [(7, 96), (33, 2240), (129, 3072), (5, 32), (300, 1152)])
+@pytest.mark.parametrize("T,d", [(7, 96), (33, 2240), (129, 3072), (5, 32), (300, 1152), (2048, 16416)])
 def test_stream_probe_digest(T, d):
     """kq_stream_probe moves the default kernel's traffic with no arithmetic: its record for each
     32-channel block is the XOR of the block's four 16-byte quarters and its scale byte the record's
     first byte.  Checked against that host evaluation on every block, ragged last units included, so
     the probe (and the unit, phase and lane addressing it shares with the quantizer) touches every
-    block exactly once and in place."""
+    block exactly once and in place.  The last shape (67.2 MB of X) is past the 64 MiB from which the
+    probe stores at device scope; the others store with the default policy."""
     rng = np.random.default_rng(T * 7 + d)
     X = rng.integers(0, 1 << 16, size=(T, d), dtype=np.uint16)
     Xd = dev(X)
@@ -448,6 +449,23 @@ def test_full_workloads(spec):
         rep = compare(codes, scales, ref["codes"], ref["scales"], yhat_fn(oracle.KRON, X, P, pstride))
         record(f"{spec.name} {variant}", rep)
         assert rep.ok(), f"{spec.name} {variant}: {rep}"
+
+
+def test_full_sana_x2_comparison_front_ends():
+    """Plain, SmoothQuant and Hadamard-32 on the whole SANA X2 matrix (4096 x 5600, 22.9 M elements,
+    46 MB of X): SmoothQuant runs block per lane there (from 2^24 elements) with the default store
+    policy (below 64 MiB of X), a kernel no other full-size case reaches."""
+    spec = next(s for s in synth.CONFIGS[2] if s.T * s.d >= (1 << 24))
+    assert spec.T * spec.d * 2 < (64 << 20)
+    X = synth.matrix(spec)
+    m = synth.smooth_mult(X)
+    for front in (1, 2, 3):
+        of = ORACLE_FRONT[front]
+        ref = oracle_ref(of, X, m=m if front == 2 else None)
+        codes, scales, _ = run_front(front, X, m if front == 2 else None)
+        rep = compare(codes, scales, ref["codes"], ref["scales"], yhat_fn(of, X, m=m if front == 2 else None))
+        record(f"{spec.name} {['kron', 'plain', 'smooth', 'hadamard'][front]}", rep)
+        assert rep.ok(exact=front != 3), str(rep)
 
 
 @pytest.mark.parametrize("spec", synth.CONFIGS[3], ids=lambda s: s.name)
