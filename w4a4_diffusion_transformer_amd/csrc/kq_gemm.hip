@@ -244,7 +244,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int m0, int n0, uin
 #pragma unroll
     for (int j = 0; j < 2; ++j) sb[j] = fix(rb[j][k], n0 + 64 * wn + 32 * j + fr == g.N - 1, pb);
     // The loads of stage ks + 3 go out one at a time, each after a second
-    // MFMA, instead of as one burst after the barrier (1.5-2% faster at the
+    // MFMA, instead of as one burst after the barrier (1-2% faster at the
     // FLUX shapes, measured on MI355X).
 #pragma unroll
     for (int s = 0; s < 2; ++s)
