@@ -117,3 +117,90 @@ def test_fixed_window_is_sound_for_the_workloads(spec):
     live = amax >= 2.0 ** -97
     w = (27.2 * norm_a(Pc)[None] * mx / np.where(live, amax, 1) + 1.1) * U * 1.01
     assert np.all(w[live] <= 2.0 ** -16), f"{spec.name}: window 2^{np.log2(w[live].max()):.2f}"
+
+
+# ---------------------------------------------------------------- the per-block refinement
+
+def near_pow2(amax32):
+    """The kernel's 2^-16 pre-filter on an fp32 amax (exponent field >= 2)."""
+    b = np.asarray(amax32, dtype=np.float32).view(np.uint32)
+    ex, mant = b >> 23, b & 0x7FFFFF
+    return (ex >= 2) & ((mant < (1 << 7)) | (mant >= (1 << 23) - (1 << 8)))
+
+
+def straddle_decision(amax32, xbits, P):
+    """The kernel's refinement of a near block, in fp32 as the kernel forms it:
+    True where the block is sent to the exact path.  amax32 [n] float32, xbits
+    [n, 32] bf16 bits, P [n, 5, 3]."""
+    f = np.float32
+    amax32 = np.asarray(amax32, dtype=f)
+    mx = ((np.max(xbits & 0x7FFF, axis=1).astype(np.uint32)) << 16).view(f)
+    l, a, b = (np.abs(P[:, :, i]).astype(f) for i in range(3))
+    na = np.ones(len(amax32), f)
+    for k in range(5):
+        r0 = a[:, k] * (f(1) + l[:, k])
+        r1 = b[:, k] + (f(1) + a[:, k] * b[:, k] * l[:, k]) * (f(1) / a[:, k])
+        na = na * np.maximum(r0, r1)
+    err = (f(27.2) * na * mx + f(1.1) * amax32) * f(2.0 ** -24) * f(1.01)
+    bits = amax32.view(np.uint32)
+    pe = np.where((bits & 0x7FFFFF) < (1 << 7), bits >> 23, (bits >> 23) + 1)
+    p2 = (np.minimum(pe, 254).astype(np.uint32) << 23).view(f)
+    with np.errstate(invalid="ignore", over="ignore"):
+        far = np.abs(amax32 - p2) > err
+    return (pe >= 255) | ~(amax32 >= f(2.0 ** -100)) | ~far
+
+
+@pytest.mark.parametrize("sigma", [0.1, 0.5])
+def test_refinement_sends_every_straddling_block_to_the_exact_path(sigma):
+    """Blocks whose exact amax is within 2^-20 of a power of two (both sides),
+    through the kernel's fp32 transform (emulated): wherever its scale differs
+    from the oracle's, the 2^-16 pre-filter and the per-block refinement both
+    send the block to the exact path."""
+    import near_blocks as nbk
+    T, nb = 8, 36
+    X, P, near = nbk.near_matrix_kron(T, nb, seed=21 + int(10 * sigma), sigma=sigma)
+    ref = oracle.quantize_rows(oracle.KRON, X, P, want_y=True)
+    y = emulate_kernel(bf16_to_f32(X), P.reshape(nb, 5, 3))
+    amax32 = np.abs(y).reshape(T, nb, 32).max(axis=2).astype(np.float32)
+    e_kernel = np.floor(np.log2(amax32.astype(np.float64))).astype(np.int64) - 2 + 127
+    straddle = (e_kernel != ref["scales"].reshape(T, nb).astype(np.int64)) & near
+    assert straddle.sum() > 0
+    Pb = np.broadcast_to(P.reshape(nb, 5, 3)[None], (T, nb, 5, 3)).reshape(-1, 5, 3)
+    sent = near_pow2(amax32).reshape(-1) & straddle_decision(amax32.reshape(-1), X.reshape(-1, 32), Pb)
+    assert np.all(sent[straddle.reshape(-1)])
+
+
+def test_refinement_follows_the_bound():
+    """The refinement's fp32 decision against the bound evaluated in fp64, for
+    real blocks of the FLUX X1 workload given amax values at chosen distances
+    from a power of two: it answers yes within the bound's distance, no beyond
+    it (outside a relative 1e-3 band at the threshold), and it lets most
+    blocks of the pre-filter's window (about three in four) skip the exact
+    path."""
+    spec = synth.CONFIGS[3][0]
+    T, nb = 16, spec.d // 32
+    X = synth.matrix(spec)[:T]
+    P = synth.params(spec).reshape(nb, 5, 3)
+    xb = X.reshape(-1, 32)
+    Pb = np.broadcast_to(P[None], (T, nb, 5, 3)).reshape(-1, 5, 3)
+    mx = np.abs(bf16_to_f32(xb).astype(np.float64)).max(axis=1)
+    na = np.repeat(norm_a(P)[None], T, axis=0).reshape(-1)
+    # each block's amax moved to a distance drawn uniformly from the pre-filter's window, at the
+    # power of two nearest its exact amax (as near blocks of the workload fall)
+    a_exact = np.abs(oracle.quantize_rows(oracle.KRON, X, P.reshape(-1), want_y=True)["yhat"]).reshape(-1, 32).max(axis=1)
+    rng = np.random.default_rng(5)
+    p = np.round(np.log2(a_exact))
+    side = np.where(rng.random(len(xb)) < 0.5, -1.0, 1.0)
+    delta = rng.uniform(2.0 ** -26, 2.0 ** -16.2, len(xb))
+    amax = (2.0 ** p * (1 + side * delta)).astype(np.float32)
+    assert near_pow2(amax).all()
+    dist = np.abs(amax.astype(np.float64) - 2.0 ** p)
+    bound = (27.2 * na * mx + 1.1 * amax.astype(np.float64)) * U * 1.01
+    got = straddle_decision(amax, xb, Pb)
+    clear = np.abs(dist / bound - 1) > 1e-3
+    np.testing.assert_array_equal(got[clear], (dist <= bound)[clear])
+    assert 0.5 < (~got).mean() < 0.95
+    # a plausible mistake, N_A left out: it would skip blocks the bound does not clear
+    wrong = dist > (27.2 * mx + 1.1 * amax.astype(np.float64)) * U * 1.01
+    assert np.any(wrong & (dist <= bound))
+

@@ -198,6 +198,46 @@ __device__ __forceinline__ void exact_block(const uint8_t* stage, int b, const f
   if (ys && lane < 32) ys[c] = y;
 }
 
+// Whether a KRON block whose fp32 amax lies within 2^-16 of a power of two
+// (near_pow2) can have its exact amax on the other side of it.  The fp32
+// transform of a block is within 27.2 u N_A max|x| of the exact sum (u =
+// 2^-24; N_A = prod_k max row sum of |D_k||U_k||L_k| = [[|a|, |a||l|],
+// [|b|, (1 + |a b||l|) / |a|]]: the rounding bound of the five shear pairs,
+// the coefficient a b and the diagonal), and the exact amax rounds to fp32
+// within 1.1 u amax; so only a block whose amax is within that distance of
+// the power of two (times 1.01, which covers this evaluation's own
+// roundings) needs its exact values.  Blocks outside the range where the
+// bound holds as stated (amax below 2^-100, where products may be
+// subnormal; a power of two at the top of the fp32 range; non-finite
+// values) always answer yes.  The block's bf16 words are read from the
+// stage; p15: its 15 scalars.
+__device__ __forceinline__ bool straddle_possible(float amax, const uint8_t* stage, int lane, const float* p15) {
+  // largest bf16 magnitude of the block: packed 16-bit maxima of the words
+  // with their sign bits cleared (integer order is magnitude order); one
+  // quarter at a time, so that the path needs few registers
+  typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
+  u16x2 m = {0, 0};
+#pragma unroll 1
+  for (int qq = 0; qq < 4; ++qq) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(stage + 16 * chunk_pos(lane, qq));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, x[e] & 0x7FFF7FFFu));
+  }
+  const float mx = fmaxf(__uint_as_float((unsigned)m[0] << 16), __uint_as_float((unsigned)m[1] << 16));
+  // (the reciprocal's ulp, like every rounding here, is inside the 1.01 margin)
+  float na = 1.0f;
+#pragma unroll 1
+  for (int k = 0; k < 5; ++k) {
+    const float l = fabsf(p15[3 * k]), a = fabsf(p15[3 * k + 1]), b = fabsf(p15[3 * k + 2]);
+    na *= fmaxf(a * (1.0f + l), b + (1.0f + a * b * l) * __builtin_amdgcn_rcpf(a));
+  }
+  const float err = (27.2f * na * mx + 1.1f * amax) * 0x1p-24f * 1.01f;
+  const unsigned ab = __float_as_uint(amax);
+  const unsigned pe = (ab & 0x7FFFFFu) < kNearLoMant ? ab >> 23 : (ab >> 23) + 1u;  // the power of two's exponent field
+  if (pe >= 255u || !(amax >= 0x1p-100f)) return true;
+  return !(fabsf(amax - __uint_as_float(pe << 23)) > err);  // a NaN err answers yes
+}
+
 template <int FRONT>
 __device__ __attribute__((noinline)) void exact_block_call(const uint8_t* stage, int b, const float* p15, int lane,
                                                            unsigned* res, float* ys) {
@@ -491,9 +531,15 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
         // exact values, one at a time by the whole wave, after the packing
         // above (so that y need not stay in registers along this path).
         const bool zero = amax == 0.0f;
-        const bool near = near_pow2(amax);
+        bool near = near_pow2(amax);
         if (__builtin_expect(__builtin_amdgcn_ballot_w64(zero || near) != 0, 0)) {
           if (zero) cw = u32x4{0u, 0u, 0u, 0u};
+          if constexpr (FRONT == FRONT_KRON) {
+            // most near blocks are far enough from the power of two for the
+            // transform's error bound to settle them (about 3 in 4 on the
+            // DiT workloads); the rest take the exact path
+            if (near) near = straddle_possible(amax, stage, lane, lds_p[wv][lane]);
+          }
           const uint64_t nearm = __builtin_amdgcn_ballot_w64(near);
           if (nearm != 0) {
             if constexpr (FRONT == FRONT_ADALN) {
