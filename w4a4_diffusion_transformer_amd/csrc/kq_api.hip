@@ -231,8 +231,7 @@ kq_status run(int front, const uint16_t* X, int64_t tokens, int64_t d, const flo
   // is the faster layout (measured on MI355X at the PixArt, SANA, FLUX and stress matrices): plain
   // and Hadamard-32 at every shape, SmoothQuant from 2^24 elements on (below that, its 32
   // multipliers per lane make the per-wave setup cost more than the row layout of kq_quad.hip).
-  const bool flat = front == kq::FRONT_KRON || front == kq::FRONT_PLAIN ||
-                    (front == kq::FRONT_HADAMARD && hblock == 32) ||
+  const bool flat = front == kq::FRONT_KRON || front == kq::FRONT_PLAIN || front == kq::FRONT_HADAMARD ||
                     (front == kq::FRONT_SMOOTH && T * d >= (int64_t(1) << 24));
   if (flat) {
     kq::FlatArgs a{};
@@ -243,6 +242,12 @@ kq_status run(int front, const uint16_t* X, int64_t tokens, int64_t d, const flo
       a.mscale = mod->mscale;
       a.mshift = mod->mshift;
       a.tps = mod->tps;
+    }
+    if (front == kq::FRONT_HADAMARD && hblock > 32) {  // stages between lanes for the bits past 32
+      front = kq::FRONT_HADAMARD_WIDE;
+      a.hlog = 6;
+      while ((1 << a.hlog) < hblock) ++a.hlog;
+      a.hscale = (float)(1.0 / std::sqrt((double)hblock));
     }
     a.X = X;
     a.T = T;
@@ -255,9 +260,6 @@ kq_status run(int front, const uint16_t* X, int64_t tokens, int64_t d, const flo
     return from_hip(kq::launch_flat(front, Y != nullptr, a, stream));
   }
   kq::QuadArgs a{};
-  a.hlog = 5;
-  while ((1 << a.hlog) < hblock) ++a.hlog;
-  a.hscale = (float)(1.0 / std::sqrt((double)hblock));
   a.X = X;
   a.T = T;
   a.d = (int)d;

@@ -25,6 +25,8 @@ enum { FRONT_KRON = 0, FRONT_PLAIN = 1, FRONT_SMOOTH = 2, FRONT_HADAMARD = 3 };
 enum { FRONT_PROBE = 4 };
 // KroQuant with the AdaLN producer step in front of the transform (block-per-lane kernel).
 enum { FRONT_ADALN = 5 };
+// Block-Hadamard of 64 .. 512 channels (block-per-lane kernel; FRONT_HADAMARD is B = 32).
+enum { FRONT_HADAMARD_WIDE = 6 };
 enum { LAYOUT_MFMA = 0, LAYOUT_QUAD = 1 };
 
 // Half-width of the window around a power of two inside which a block's
@@ -171,45 +173,6 @@ struct ExactFromSplit {
       s = fma(x, (double)k, s);
     }
     return (float)s;
-  }
-};
-
-// Block-Hadamard column: (sum_r (-1)^popcount(r & c) x[r]) / sqrt(32) in
-// fp64 (sum from +0 in input order), rounded once to fp32.
-struct ExactHadamard {
-  __device__ float operator()(const uint16_t* __restrict__ xblk, int c) const {
-    double s = 0.0;
-#pragma unroll 1
-    for (int r = 0; r < 32; ++r) {
-      const double x = (double)__uint_as_float((unsigned)xblk[r] << 16);
-      s = s + ((__popc(r & c) & 1) ? -x : x);
-    }
-    return (float)(s / 5.6568542494923801952067548968387923142786875015078);
-  }
-};
-
-// Block-Hadamard column for block sizes B = 32 .. 512: the same fp64 sum over
-// the B inputs of the Hadamard block (input order), divided once by sqrt(B).
-// xB points at the B-block's first input, off is this 32-block's offset in it.
-struct ExactHadamardB {
-  const uint16_t* xB;
-  int B;
-  int off;
-  __device__ float operator()(const uint16_t* __restrict__, int c) const {
-    const int col = off + c;
-    double s = 0.0;
-#pragma unroll 1
-    for (int r = 0; r < B; ++r) {
-      const double x = (double)__uint_as_float((unsigned)xB[r] << 16);
-      s = s + ((__popc(r & col) & 1) ? -x : x);
-    }
-    // sqrt(B) for B = 32, 64, 128, 256, 512, each correctly rounded
-    const double sq = B == 32    ? 5.6568542494923801952067548968387923142786875015078
-                      : B == 64  ? 8.0
-                      : B == 128 ? 11.313708498984760390413509793677584628557375003016
-                      : B == 256 ? 16.0
-                                 : 22.627416997969520780827019587355169257114750006031;
-    return (float)(s / sq);
   }
 };
 

@@ -31,10 +31,17 @@
 // multiply by the product of the five diagonals.  All in fp32; the error
 // against the exact sum stays well below 1e-5 of the block amax.
 // FRONT_PLAIN: y = x.  FRONT_SMOOTH: y = x * m[c].  FRONT_HADAMARD: the
-// 32-point Walsh-Hadamard butterflies, then / sqrt(32).  FRONT_ADALN: the
+// 32-point Walsh-Hadamard butterflies, then / sqrt(32).  FRONT_HADAMARD_WIDE:
+// blocks of B = 64 .. 512 channels, i.e. of B / 32 consecutive lanes (a
+// unit's 64 blocks start on a multiple of B / 32 and rows hold whole
+// Hadamard blocks): the 32-point stages in the lane, then one stage per
+// channel bit 5 .. log2 B - 1 between lanes 1, 2, 4, 8 apart, then
+// / sqrt(B).  FRONT_ADALN: the
 // AdaLN producer step, then KRON (below, at modulate32).  FRONT_PROBE: the
 // same loads, LDS round trip and stores with no arithmetic (a bandwidth
 // ceiling for this access pattern; its outputs are a digest, not codes).
+#include <type_traits>
+
 #include "kq_device.hpp"
 #include "kq_internal.h"
 
@@ -83,6 +90,14 @@ __device__ __forceinline__ float max32(float v) {
   const unsigned u = __float_as_uint(v);
   const auto sw = __builtin_amdgcn_permlane16_swap(u, u, false, false);  // rows 0 <-> 1, 2 <-> 3
   return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+// v of lane ^ M (M = 1, 2: DPP quad permutes; 4, 8: swizzle within 32 lanes)
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) {
+  if constexpr (M == 1) return dpp_f<0xB1>(v);  // quad_perm [1,0,3,2]
+  else if constexpr (M == 2) return dpp_f<0x4E>(v);  // quad_perm [2,3,0,1]
+  else return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (M << 10) | 0x1F));
 }
 
 // The AdaLN producer step of one block (the handbook page "Quantization:
@@ -244,6 +259,45 @@ __device__ __attribute__((noinline)) void exact_block_call(const uint8_t* stage,
   exact_block<FRONT>(stage, b, p15, lane, res, ys);
 }
 
+// The exact path of FRONT_HADAMARD_WIDE: block b of the staged unit, one
+// of the B / 32 blocks (lanes) of its Hadamard block.  Lane c (mod 32)
+// computes the block's channel c as the fp64 sum, from +0 in input order,
+// of (-1)^popcount(r & col) x[r] over the Hadamard block's B inputs (col:
+// the channel's index in the Hadamard block), divided once by sqrt(B) and
+// rounded to fp32; then as exact_block.
+__device__ __attribute__((noinline)) void exact_block_wide(const uint8_t* stage, int b, int hlog, int lane,
+                                                           unsigned* res, float* ys) {
+  const int c = lane & 31;
+  const int g = 1 << (hlog - 5);
+  const int b0 = b & ~(g - 1);
+  const int col = 32 * (b - b0) + c;
+  double s = 0.0;
+#pragma unroll 1
+  for (int k = 0; k < g; ++k)
+#pragma unroll
+    for (int qq = 0; qq < 4; ++qq) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(stage + 16 * chunk_pos(b0 + k, qq));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 32 * k + 8 * qq + e;
+        const double x = (double)((e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]));
+        s = s + ((__popc(r & col) & 1) ? -x : x);
+      }
+    }
+  // sqrt(B) for B = 64, 128, 256, 512, each correctly rounded
+  const double sq = hlog == 6 ? 8.0
+                    : hlog == 7 ? 11.313708498984760390413509793677584628557375003016
+                    : hlog == 8 ? 16.0
+                                : 22.627416997969520780827019587355169257114750006031;
+  const float y = (float)(s / sq);
+  const unsigned byte = e8m0_byte(max32(fabsf(y)));
+  const float y1 = dpp_f<0xB1>(y);
+  const unsigned pair = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y, y1, __uint_as_float(byte << 23), 0) & 0xFFu;
+  if (lane < 32 && !(c & 1)) reinterpret_cast<uint8_t*>(res)[c >> 1] = (uint8_t)pair;
+  if (lane == 0) res[4] = byte;
+  if (ys && lane < 32) ys[c] = y;
+}
+
 // CPOL: the cache policy of the code and scale stores (0, or kSC1: device
 // scope, below at launch_flat).
 template <int FRONT, bool STORE_Y, int CPOL>
@@ -251,7 +305,8 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
   __shared__ __attribute__((aligned(256))) uint8_t lds_x[kWaves][kUnitBytes];
   constexpr bool kKron = FRONT == FRONT_KRON || FRONT == FRONT_ADALN;  // fronts with KroQuant's transform
   __shared__ float lds_p[kKron ? kWaves : 1][64][15];                  // exact path: each lane's 15 scalars
-  constexpr bool kSum = kKron || FRONT == FRONT_HADAMARD;              // fronts with an exact path
+  constexpr bool kHad = FRONT == FRONT_HADAMARD || FRONT == FRONT_HADAMARD_WIDE;
+  constexpr bool kSum = kKron || kHad;                                 // fronts with an exact path
   __shared__ unsigned lds_res[kSum ? kWaves : 1][64][5];   // exact path: code words and byte per lane
   __shared__ float lds_ys[kSum && STORE_Y ? kWaves : 1][32];  // exact path: the values (diagnostic Y)
 
@@ -518,6 +573,31 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
             }
 #pragma unroll
         for (int c = 0; c < 32; ++c) y[c] *= 0.17677669529663688110021109052621225982120698f;  // 1/sqrt(32)
+      } else if constexpr (FRONT == FRONT_HADAMARD_WIDE) {
+#pragma unroll
+        for (int bit = 1; bit < 32; bit <<= 1)
+#pragma unroll
+          for (int c = 0; c < 32; ++c)
+            if (!(c & bit)) {
+              const float u = y[c], v = y[c | bit];
+              y[c] = u + v;
+              y[c | bit] = u - v;
+            }
+        // channel bits 5 .. hlog - 1: the lane with the bit clear keeps own + partner, the other
+        // partner - own
+        auto cross = [&](auto m_) {
+          constexpr int M = decltype(m_)::value;
+          const float sgn = (lane & M) ? -1.0f : 1.0f;
+#pragma unroll
+          for (int c = 0; c < 32; ++c) y[c] = fmaf(y[c], sgn, lane_xor<M>(y[c]));
+        };
+        cross(std::integral_constant<int, 1>{});
+        if (a.hlog > 6) cross(std::integral_constant<int, 2>{});  // uniform
+        if (a.hlog > 7) cross(std::integral_constant<int, 4>{});
+        if (a.hlog > 8) cross(std::integral_constant<int, 8>{});
+        const float hs = a.hscale;
+#pragma unroll
+        for (int c = 0; c < 32; ++c) y[c] *= hs;
       }
 
       const float amax = absmax32(y);
@@ -559,6 +639,8 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
               if constexpr (kKron)
                 exact_block<FRONT_KRON>(stage, L, lds_p[wv][L], lane, lds_res[wv][L],
                                         STORE_Y ? lds_ys[STORE_Y ? wv : 0] : nullptr);
+              else if constexpr (FRONT == FRONT_HADAMARD_WIDE)
+                exact_block_wide(stage, L, a.hlog, lane, lds_res[wv][L], STORE_Y ? lds_ys[STORE_Y ? wv : 0] : nullptr);
               else
                 exact_block_call<FRONT>(stage, L, lds_p[0][L], lane, lds_res[wv][L],
                                         STORE_Y ? lds_ys[STORE_Y ? wv : 0] : nullptr);
@@ -674,6 +756,7 @@ hipError_t launch_flat(int front, bool store_y, const FlatArgs& args, hipStream_
     case FRONT_PLAIN: fn = big ? pick<FRONT_PLAIN, kSC1>(store_y) : pick<FRONT_PLAIN, 0>(store_y); break;
     case FRONT_SMOOTH: fn = big ? pick<FRONT_SMOOTH, kSC1>(store_y) : pick<FRONT_SMOOTH, 0>(store_y); break;
     case FRONT_HADAMARD: fn = pick<FRONT_HADAMARD, kSC1>(store_y); break;
+    case FRONT_HADAMARD_WIDE: fn = pick<FRONT_HADAMARD_WIDE, kSC1>(store_y); break;
     case FRONT_PROBE:
       fn = big ? (const void*)&flat_kernel<FRONT_PROBE, false, kSC1> : (const void*)&flat_kernel<FRONT_PROBE, false, 0>;
       break;

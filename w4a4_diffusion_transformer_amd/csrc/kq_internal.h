@@ -55,8 +55,6 @@ struct QuadArgs {
   uint8_t* codes;
   uint8_t* scales;
   float* Y;
-  int hlog;        // Hadamard front-end: log2 of the block size (5 .. 9)
-  float hscale;    // and 1 / sqrt(block size) in fp32
   int ngroups, nchunks;
 };
 
@@ -84,6 +82,8 @@ struct FlatArgs {
   int phases, chunks;
   int rows_step;      // set by launch_flat: rows between a lane's consecutive blocks
   int req_waves = 0;  // requested total waves (tuning; 0: one resident round)
+  int hlog = 5;       // FRONT_HADAMARD_WIDE: log2 of the Hadamard block (6 .. 9)
+  float hscale = 0.0f;  // and 1 / sqrt(block) in fp32
 };
 
 // Compute units of the current device (cached per device).

@@ -1,18 +1,17 @@
-// Vector-ALU comparison front-ends fused with the MXFP4 quantizer (gfx950):
+// Vector-ALU comparison front-ends fused with the MXFP4 quantizer (gfx950),
+// row layout:
 //   FRONT_PLAIN     y = x;
-//   FRONT_SMOOTH    y = x * m[c] (SmoothQuant per-channel scale);
-//   FRONT_HADAMARD  y = (x H_B)[c] / sqrt(B), fast Walsh-Hadamard butterflies
-//                   over blocks of B = 32 .. 512 channels (stages on channel
-//                   bits 5 and up pair lanes 4, 8, 16, 32 apart).
+//   FRONT_SMOOTH    y = x * m[c] (SmoothQuant per-channel scale).
+// The library runs SmoothQuant here below 2^24 elements, where its 8
+// multipliers per lane cost less setup than the block-per-lane kernel's 32
+// (kq_flat.hip holds every other front-end).
 //
 // Lane layout: a wave covers 1 KB of one bf16 row (16 blocks); lane l owns
 // the fixed 16-byte piece l, i.e. channels 8q .. 8q+7 (q = l & 3) of block
 // l >> 2 of its column group, for every row it visits.  Loads (1 KB), code
 // stores (256 B) and scale stores (16 B) of a wave instruction are therefore
 // contiguous, and each lane keeps the multipliers of a single block in
-// registers.  Hadamard stages on channel bits 0-2 stay in registers; bits 3
-// and 4 pair lane l with l^1 and l^2 (the four lanes of a block), exchanged
-// with DPP quad permutes.  Rows stream with loads kept several rows ahead.
+// registers.  Rows stream with loads kept several rows ahead.
 #include "kq_device.hpp"
 #include "kq_internal.h"
 
@@ -22,31 +21,6 @@ namespace {
 
 constexpr int kWaves = 4;  // waves per workgroup, one row each per step
 constexpr int kDepth = 6;  // rows in flight per wave (current + 5 ahead)
-
-template <int XOR>
-__device__ __forceinline__ float partner(float v) {
-  if constexpr (XOR == 1) return dpp_quad_xor1(v);
-  else return dpp_quad_xor2(v);
-}
-
-// Walsh-Hadamard butterflies: (a, b) -> (a + b, a - b).
-template <int BIT>
-__device__ __forceinline__ void wht_in_reg(float v[8]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (i & BIT) continue;
-    const float a = v[i], b = v[i | BIT];
-    v[i] = a + b;
-    v[i | BIT] = a - b;
-  }
-}
-
-// Lane with bit value beta: beta = 0 keeps own + partner, beta = 1 partner - own.
-template <int XOR>
-__device__ __forceinline__ void wht_cross(float v[8], float sgn) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = fmaf(v[i], sgn, partner<XOR>(v[i]));
-}
 
 __device__ __forceinline__ void unpack8(const u32x4& w, float v[8]) {
 #pragma unroll
@@ -80,7 +54,6 @@ __global__ __launch_bounds__(64 * kWaves) void quad_kernel(QuadArgs a) {
       mult[4 + i] = m1[i];
     }
   }
-  const float sgn3 = (q & 1) ? -1.0f : 1.0f, sgn4 = (q >> 1) ? -1.0f : 1.0f;
 
   const int64_t d = a.d;
   const int nrb = (a.T + kWaves - 1) / kWaves;  // row blocks of kWaves rows
@@ -122,33 +95,11 @@ __global__ __launch_bounds__(64 * kWaves) void quad_kernel(QuadArgs a) {
     if constexpr (FRONT == FRONT_SMOOTH) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) y[i] *= mult[i];
-    } else if constexpr (FRONT == FRONT_HADAMARD) {
-      wht_in_reg<1>(y);
-      wht_in_reg<2>(y);
-      wht_in_reg<4>(y);
-      wht_cross<1>(y, sgn3);
-      wht_cross<2>(y, sgn4);
-      // channel bits 5 .. hlog-1 (blocks of 64 .. 512): bit b of the channel is bit b-3 of the lane
-#pragma unroll 1
-      for (int bt = 5; bt < a.hlog; ++bt) {
-        const int m = 1 << (bt - 3);
-        const float sgn = (lane & m) ? -1.0f : 1.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) y[i] = fmaf(y[i], sgn, __shfl_xor(y[i], m, 64));
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) y[i] *= a.hscale;
     }
-    // rows past the end hold zeros (amax 0): the exact path never runs for them
+    // (plain and SmoothQuant values are exact in fp32: no exact-scale path)
     const uint16_t* xblk = (in ? cx : a.X) + 32 * jc;
     unsigned word, byte;
-    if constexpr (FRONT == FRONT_HADAMARD) {
-      const int hb = 1 << a.hlog;
-      const int off = (32 * jc) & (hb - 1);
-      mx_epilogue<LAYOUT_QUAD, true>(y, xblk, q, ExactHadamardB{xblk - off, hb, off}, word, byte);
-    } else {
-      mx_epilogue<LAYOUT_QUAD, false>(y, xblk, q, NoExact{}, word, byte);
-    }
+    mx_epilogue<LAYOUT_QUAD, false>(y, xblk, q, NoExact{}, word, byte);
     __builtin_amdgcn_raw_buffer_store_b32(word, rsrc(cc, in ? crow_bytes : 0), coff, 0, 0);
     __builtin_amdgcn_raw_buffer_store_b8((uint8_t)byte, rsrc(cs, in ? srow_bytes : 0), soff, 0, 0);
     if constexpr (STORE_Y) {
@@ -191,7 +142,6 @@ hipError_t launch_quad(int front, bool store_y, const QuadArgs& args, hipStream_
   switch (front) {
     case FRONT_PLAIN: fn = pick<FRONT_PLAIN>(store_y); break;
     case FRONT_SMOOTH: fn = pick<FRONT_SMOOTH>(store_y); break;
-    case FRONT_HADAMARD: fn = pick<FRONT_HADAMARD>(store_y); break;
     default: return hipErrorInvalidValue;
   }
   QuadArgs a = args;
