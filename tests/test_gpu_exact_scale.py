@@ -109,6 +109,32 @@ def test_hadamard_scales_exact_near_powers_of_two(B):
     assert rep.code_unexplained == 0, str(rep)
 
 
+@pytest.mark.parametrize("B", [64, 512])
+def test_hadamard_exact_path_wide_exponent_range(B):
+    """Near-power-of-two Hadamard blocks whose inputs also hold values of about 2^-100: the exponent
+    range then exceeds what makes every fp64 partial sum exact, so the kernel takes the sequential
+    fp64 sum over the Hadamard block instead of the fp64 butterflies; scales must still equal the
+    oracle's, and codes differ only at classified ties."""
+    X, near = nbk.near_matrix_hadamard(16, 2048, B, seed=300 + B)
+    X = X.copy()
+    tiny = synth.f32_to_bf16(np.array([2.0 ** -100, -(2.0 ** -100)], dtype=np.float32))
+    X[:, 5::97] = tiny[0]  # one or two tiny inputs in every Hadamard block, far from the block amax
+    X[:, 11::131] = tiny[1]
+    ref = oracle.quantize_rows_hadamard(X, B, want_y=True)
+    Xd = dev(X)
+    codes, scales = kq.alloc_outputs(Xd)
+    kq.kq_hadamard_quantize_ex(Xd, B, codes, scales)
+    torch.cuda.synchronize()
+    c, s = codes.cpu().numpy(), scales.cpu().numpy()
+    np.testing.assert_array_equal(s, ref["scales"])
+
+    def yh(rows):
+        return ref["yhat"][rows], ref["y32"][rows]
+
+    rep = compare(c, s, ref["codes"], ref["scales"], yh)
+    assert rep.code_unexplained == 0, str(rep)
+
+
 def convert_sweep_values(rng) -> np.ndarray:
     """fp32 values in (-8, 8): every fp32 within 2^12 ulps of each E2M1 midpoint
     (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5), each grid value +- a few ulps, and

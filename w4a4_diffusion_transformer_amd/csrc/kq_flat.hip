@@ -299,6 +299,83 @@ __device__ __attribute__((noinline)) void exact_block_wide(const uint8_t* stage,
   if (ys && lane < 32) ys[c] = y;
 }
 
+// The same values by the fp64 fast Walsh-Hadamard transform, when it is
+// provably the same: every input is a bf16, an integer multiple of 2^(e' -
+// 134) with e' = max(e, 1) its exponent field, so every partial sum of the
+// Hadamard block is an integer multiple of 2^(min e' - 134) of magnitude below
+// B 2^(max e' - 126); when max e' - min e' <= 45 - log2 B (nonzero inputs, no
+// infinity or NaN) those integers fit in 53 bits, every sum is exact in fp64,
+// and the butterflies give exactly the sequential sum.  Layout: lane l holds
+// inputs 8 l .. 8 l + 7 of the Hadamard block (in-lane stages on bits 0-2,
+// then stages between lanes 1, 2, 4, 8, 16, 32 apart), so block b's values are
+// on lanes 4 (b - b0) .. + 3, which quantize them as the exact path's result.
+// Returns false (nothing written) when the exponent range is too wide.
+__device__ __attribute__((noinline)) bool exact_block_wide_fast(const uint8_t* stage, int b, int hlog, int lane,
+                                                                unsigned* res) {
+  const int g = 1 << (hlog - 5);
+  const int b0 = b & ~(g - 1);
+  const bool in = lane < 4 * g;
+  const u32x4 w = in ? *reinterpret_cast<const u32x4*>(stage + 16 * chunk_pos(b0 + (lane >> 2), lane & 3))
+                     : u32x4{0u, 0u, 0u, 0u};
+  int emax = 0, emin = 255;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const unsigned h = (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+    if (h & 0x7FFFu) {
+      const int e = max((int)((h >> 7) & 0xFFu), 1);
+      emax = max(emax, e);
+      emin = min(emin, e);
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    emax = max(emax, __shfl_xor(emax, m, 64));
+    emin = min(emin, __shfl_xor(emin, m, 64));
+  }
+  if (emax == 255 || emax - emin > 45 - hlog) return false;  // uniform
+  double v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = (double)((k & 1) ? bf16_hi(w[k >> 1]) : bf16_lo(w[k >> 1]));
+#pragma unroll
+  for (int bit = 1; bit < 8; bit <<= 1)
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (!(k & bit)) {
+        const double a0 = v[k], a1 = v[k | bit];
+        v[k] = a0 + a1;
+        v[k | bit] = a0 - a1;
+      }
+  for (int m = 1; m < 4 * g; m <<= 1) {  // uniform
+    const bool hi = lane & m;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const double o = __shfl_xor(v[k], m, 64);
+      v[k] = hi ? o - v[k] : v[k] + o;
+    }
+  }
+  // sqrt(B), correctly rounded, as the sequential path divides by it
+  const double sq = hlog == 6 ? 8.0
+                    : hlog == 7 ? 11.313708498984760390413509793677584628557375003016
+                    : hlog == 8 ? 16.0
+                                : 22.627416997969520780827019587355169257114750006031;
+  float y[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) y[k] = (float)(v[k] / sq);
+  // block b: lanes 4 (b - b0) .. + 3, channels 8 (lane & 3) .. + 7
+  float a = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) a = fmaxf(a, fabsf(y[k]));
+  a = fmaxf(a, __shfl_xor(a, 1, 64));
+  a = fmaxf(a, __shfl_xor(a, 2, 64));
+  const unsigned byte = e8m0_byte(a);
+  const unsigned word = pack_fp4(y, byte);
+  if ((lane >> 2) == b - b0) {
+    res[lane & 3] = word;
+    if ((lane & 3) == 0) res[4] = byte;
+  }
+  return true;
+}
+
 // CPOL: the cache policy of the code and scale stores (0, or kSC1: device
 // scope, below at launch_flat).
 template <int FRONT, bool STORE_Y, int CPOL>
@@ -640,8 +717,10 @@ __global__ __launch_bounds__(64 * kWaves) void flat_kernel(FlatArgs a) {
               if constexpr (kKron)
                 exact_block<FRONT_KRON>(stage, L, lds_p[wv][L], lane, lds_res[wv][L],
                                         STORE_Y ? lds_ys[STORE_Y ? wv : 0] : nullptr);
-              else if constexpr (FRONT == FRONT_HADAMARD_WIDE)
-                exact_block_wide(stage, L, a.hlog, lane, lds_res[wv][L], STORE_Y ? lds_ys[STORE_Y ? wv : 0] : nullptr);
+              else if constexpr (FRONT == FRONT_HADAMARD_WIDE) {
+                if (STORE_Y || !exact_block_wide_fast(stage, L, a.hlog, lane, lds_res[wv][L]))
+                  exact_block_wide(stage, L, a.hlog, lane, lds_res[wv][L], STORE_Y ? lds_ys[STORE_Y ? wv : 0] : nullptr);
+              }
               else
                 exact_block_call<FRONT>(stage, L, lds_p[0][L], lane, lds_res[wv][L],
                                         STORE_Y ? lds_ys[STORE_Y ? wv : 0] : nullptr);
